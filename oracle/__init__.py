@@ -1,0 +1,250 @@
+"""CPU oracle for microscaling quantization and the block-scaled linear layer.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the product path
+(``microscaling_quantized_dit_amd``) never does and shares no code with it.
+
+The arithmetic lives in ``mxq_oracle.c`` (plain scalar C, fp64, exact
+comparisons); this module builds it with gcc on first use and wraps it for
+numpy arrays.  See the header of ``mxq_oracle.c`` for the definitions followed
+and the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+E4M3, E5M2, E2M1 = 0, 1, 2
+EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxq_oracle.c")
+_LIB = os.path.join(_HERE, "liborc.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (OpenMP, no fast-math) into oracle/liborc.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-D_GNU_SOURCE",
+               "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i64, i32, f64, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_float
+        sig = {
+            "orc_bf16_value": (f64, [ctypes.c_uint16]),
+            "orc_code_value": (f64, [i32, i32]),
+            "orc_e8m0_value": (f64, [i32]),
+            "orc_round_quotient": (i32, [i32, f64, f64]),
+            "orc_round_quotient_array": (None, [i32, P, f64, i64, P]),
+            "orc_rn_fp32_div": (f32, [f64, f64]),
+            "orc_quantize_mxfp8": (i32, [P, i64, i64, i32, P, P]),
+            "orc_nvfp4_global_scale": (f32, [P, i64]),
+            "orc_quantize_nvfp4": (i32, [P, i64, i64, P, P, P, P]),
+            "orc_dequant_mxfp8": (None, [P, P, i64, i32, P, i64, P]),
+            "orc_dequant_nvfp4": (None, [P, P, f32, i64, P, i64, P]),
+            "orc_linear": (None, [P, P, f64, P, i32, i64, i64, i64, P]),
+            "orc_max_threads": (i32, []),
+            "orc_set_threads": (None, [i32]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _as_u16(x) -> np.ndarray:
+    """bf16 bit patterns as a C-contiguous uint16 array (accepts numpy uint16/int16
+    arrays or CPU torch bfloat16 tensors)."""
+    if hasattr(x, "dtype") and str(x.dtype) == "torch.bfloat16":
+        import torch
+        x = x.detach().cpu().contiguous().view(torch.int16).numpy()
+    a = np.ascontiguousarray(x)
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected bf16 bit patterns (uint16), got %s" % a.dtype)
+    return a
+
+
+# ------------------------------------------------------------------ formats
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(bits)
+
+
+def code_value(fmt: int, code: int) -> float:
+    return _load().orc_code_value(fmt, code)
+
+
+def e8m0_value(code: int) -> float:
+    return _load().orc_e8m0_value(code)
+
+
+def round_quotient(fmt: int, num: float, den: float) -> int:
+    """Magnitude code of RNE_sat(num/den) (num >= 0, den > 0)."""
+    return _load().orc_round_quotient(fmt, num, den)
+
+
+def round_quotient_array(fmt: int, num: np.ndarray, den: float) -> np.ndarray:
+    num = np.ascontiguousarray(num, dtype=np.float64)
+    out = np.empty(num.shape, np.uint8)
+    _load().orc_round_quotient_array(fmt, _ptr(num), den, num.size, _ptr(out))
+    return out
+
+
+def rn_fp32_div(a: float, d: float) -> np.float32:
+    return np.float32(_load().orc_rn_fp32_div(a, d))
+
+
+# --------------------------------------------------------------- quantizers
+
+def quantize_mxfp8(x, fmt: int = E4M3):
+    """bf16 [rows, cols] -> (codes u8 [rows, cols], E8M0 scales u8 [rows, cols/32])."""
+    a = _as_u16(x)
+    rows, cols = a.shape
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((rows, cols // 32), np.uint8)
+    rc = _load().orc_quantize_mxfp8(_ptr(a), rows, cols, fmt, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("orc_quantize_mxfp8: bad arguments (rc=%d)" % rc)
+    return q, s
+
+
+def nvfp4_global_scale(x) -> np.float32:
+    a = _as_u16(x)
+    return np.float32(_load().orc_nvfp4_global_scale(_ptr(a), a.size))
+
+
+def quantize_nvfp4(x, global_scale=None):
+    """bf16 [rows, cols] -> (packed codes u8 [rows, cols/2], E4M3 scales u8
+    [rows, cols/16], fp32 global decode scale).  global_scale None = dynamic."""
+    a = _as_u16(x)
+    rows, cols = a.shape
+    q = np.empty((rows, cols // 2), np.uint8)
+    s = np.empty((rows, cols // 16), np.uint8)
+    g_out = np.zeros(1, np.float32)
+    g_in = None if global_scale is None else np.array([global_scale], np.float32)
+    rc = _load().orc_quantize_nvfp4(_ptr(a), rows, cols, None if g_in is None else _ptr(g_in),
+                                    _ptr(q), _ptr(s), _ptr(g_out))
+    if rc != 0:
+        raise ValueError("orc_quantize_nvfp4: bad arguments (rc=%d)" % rc)
+    return q, s, np.float32(g_out[0])
+
+
+# -------------------------------------------------------------- dequant / GEMM
+
+def _rows(row_idx, n_all):
+    if row_idx is None:
+        return None, n_all
+    r = np.ascontiguousarray(row_idx, dtype=np.int64)
+    return r, r.size
+
+
+def dequant_mxfp8(q, s, fmt: int = E4M3, row_idx=None) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    cols = q.shape[1]
+    r, n = _rows(row_idx, q.shape[0])
+    out = np.empty((n, cols), np.float64)
+    _load().orc_dequant_mxfp8(_ptr(q), _ptr(s), cols, fmt, None if r is None else _ptr(r), n, _ptr(out))
+    return out
+
+
+def dequant_nvfp4(q, s, global_scale, row_idx=None) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    cols = q.shape[1] * 2
+    r, n = _rows(row_idx, q.shape[0])
+    out = np.empty((n, cols), np.float64)
+    _load().orc_dequant_nvfp4(_ptr(q), _ptr(s), float(global_scale), cols,
+                              None if r is None else _ptr(r), n, _ptr(out))
+    return out
+
+
+def linear(a_deq: np.ndarray, w_deq: np.ndarray, alpha: float = 1.0, bias=None,
+           epi: int = EPI_NONE) -> np.ndarray:
+    """fp64 epi(alpha * a @ w.T + bias), a [m, K], w [N, K] dequantized operands."""
+    a = np.ascontiguousarray(a_deq, np.float64)
+    w = np.ascontiguousarray(w_deq, np.float64)
+    m, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("K mismatch")
+    b = None
+    if epi != EPI_NONE:
+        b = _as_u16(bias).reshape(-1)
+        if b.size != N:
+            raise ValueError("bias must have N entries")
+    out = np.empty((m, N), np.float64)
+    _load().orc_linear(_ptr(a), _ptr(w), float(alpha), None if b is None else _ptr(b), epi, m, N, K, _ptr(out))
+    return out
+
+
+def gemm_mxfp8(a_q, a_s, w_q, w_s, a_fmt=E4M3, w_fmt=E4M3, bias=None, epi=EPI_NONE, row_idx=None):
+    """Reference output (fp64, unrounded) of C = A W^T (+bias) (GELU) for MXFP8 operands."""
+    a = dequant_mxfp8(a_q, a_s, a_fmt, row_idx)
+    w = dequant_mxfp8(w_q, w_s, w_fmt)
+    return linear(a, w, 1.0, bias, epi)
+
+
+def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=EPI_NONE, row_idx=None):
+    """Reference output (fp64, unrounded) for NVFP4 operands:
+    epi(alpha * sum_k val(qa) S_a val(qw) S_w + bias) with alpha = s_ga * s_gw.
+    Operands are dequantized without the global scales so every product is
+    exact in fp64 (6 significant bits each); alpha (48 bits) is exact too."""
+    a = dequant_nvfp4(a_q, a_s, 1.0, row_idx)
+    w = dequant_nvfp4(w_q, w_s, 1.0)
+    alpha = float(np.float64(np.float32(a_g)) * np.float64(np.float32(w_g)))
+    return linear(a, w, alpha, bias, epi)
+
+
+def max_threads() -> int:
+    return _load().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().orc_set_threads(n)
+
+
+# ------------------------------------------------------------- tolerance check
+
+def compare(gpu_bf16_values: np.ndarray, ref: np.ndarray) -> dict:
+    """Error of a bf16 GEMM output against the fp64 reference.
+
+    max_rel = max |g - r| / max(|r|, rms(r)) (the rms floor keeps cancellation
+    near zero from dominating); also the relative Frobenius error and the max
+    absolute error."""
+    g = np.asarray(gpu_bf16_values, np.float64)
+    r = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    diff = np.abs(g - r)
+    floor = np.maximum(np.abs(r), rms if rms > 0 else 1.0)
+    return {
+        "max_rel": float((diff / floor).max()) if r.size else 0.0,
+        "fro_rel": float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)) if r.size else 0.0,
+        "max_abs": float(diff.max()) if r.size else 0.0,
+        "rms_ref": rms,
+    }
