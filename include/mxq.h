@@ -1,0 +1,166 @@
+/*
+ * mxq.h -- C ABI of the microscaling-quantized linear layer for AMD MI355X (gfx950).
+ *
+ * Two parts of a quantized diffusion-transformer Linear:
+ *   1. dynamic microscaling quantizers for bf16 tensors (MXFP8, NVFP4);
+ *   2. block-scaled GEMMs that consume those codes and scales and return bf16,
+ *      optionally with a fused bias or bias + GELU (tanh form).
+ *
+ * Sources (pages, by title and section):
+ *   [P1] "NVIDIA量化推理：5步极速优化显存+成功率翻倍", section "MXFP8和NVFP4技术背景解析":
+ *        blocks of 16 or 32 values share a high-precision scale; MXFP8 (OCP) has
+ *        E4M3 and E5M2 elements; NVFP4 is E2M1 in blocks of 16 with FP8 scales.
+ *        Step 2: dynamic activation + weight quantization with a dynamic
+ *        per-tensor scale.
+ *   [P2] "NVIDIA Blackwell平台FP4量化技术解析与图像生成优化", section 3.1: the runtime
+ *        quantizer turns bf16 into [FP4 data, FP8 block scales, FP32 global
+ *        scale]; weights are quantized offline the same way.  Section 5.2:
+ *        quantization blocks aligned to multiples of 128.
+ *   [P3] "Modelos de Difusão": every torch.nn.Linear of the transformer is
+ *        quantized (nn.Linear orientation: C = A W^T).
+ *   [P4] "麦橘超然性能实战分析：float8量化如何提升GPU利用率", section 2.2: E4M3 is
+ *        1+4+3 bits, E5M2 1+5+2 bits.
+ *   [P5] "FP8量化技术提升SD3.5在低带宽环境下的响应速度", step 2: q = round(x/scale).
+ *
+ * Number formats and rounding (the pages name the formats; where they are
+ * silent these readings are taken):
+ *   - every stored quantity is ONE round-to-nearest-even of its exact value,
+ *     saturating to the largest finite magnitude (E4M3 448, E5M2 57344, E2M1 6);
+ *   - the sign bit of every element code is the sign bit of the input;
+ *   - MXFP8: per 32 consecutive values of a row, E = floor(log2 amax) - emax
+ *     (emax = 8 for E4M3, 15 for E5M2), clamped to [-127, 127], E = -127 for an
+ *     all-zero block; the E8M0 scale byte is E + 127; q = RNE_sat(x / 2^E);
+ *   - NVFP4: s_g = RN_fp32(amax_tensor / 2688) (2688 = 6 * 448; 1 if the tensor
+ *     is all zero) is the fp32 DECODE global scale; per 16 consecutive values
+ *     S_b = RN_E4M3_sat(amax_block / (6 s_g)) (may be 0); q = RN_E2M1_sat(x / (S_b s_g)),
+ *     magnitude 0 when S_b = 0; dequantized value = val(q) * val(S_b) * s_g.
+ *
+ * Layouts (all row-major, no padding):
+ *   x        bf16  [rows, cols]            cols contiguous (K for a GEMM operand)
+ *   MXFP8 q  u8    [rows, cols]            E4M3 or E5M2 codes
+ *   MXFP8 s  u8    [rows, cols / 32]       E8M0 scale bytes
+ *   NVFP4 q  u8    [rows, cols / 2]        byte j holds element 2j in its low nibble
+ *   NVFP4 s  u8    [rows, cols / 16]       E4M3 scale codes
+ *   GEMM     C[M, N] = A[M, K] * W[N, K]^T, C bf16 [M, N]
+ *
+ * Conventions:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller; the library never allocates or frees.  Base pointers must
+ *     be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = default stream).  Every call is
+ *     asynchronous on that stream and never synchronizes; outputs are valid
+ *     after the caller synchronizes the stream.
+ *   - Arguments are validated before any launch; an invalid call returns a
+ *     status and launches nothing.  mxq_last_error() gives the detail.
+ *   - Inputs must be finite (NaN/Inf inputs give unspecified codes).
+ *   - No exceptions cross the ABI; no global mutable state besides a per-thread
+ *     error string and a per-device architecture cache.
+ *   - Requires a gfx950 device (MXFP8/NVFP4 scaled MFMA); other devices get
+ *     MXQ_ERROR_UNSUPPORTED_DEVICE.
+ */
+#ifndef MXQ_H_
+#define MXQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXQ_SUCCESS = 0,
+  MXQ_ERROR_INVALID_VALUE = 1,     /* null pointer, non-positive size, bad enum */
+  MXQ_ERROR_UNSUPPORTED_SHAPE = 2, /* size not a multiple of the block / tile rule */
+  MXQ_ERROR_MISALIGNED = 3,        /* a base pointer is not 16-byte aligned */
+  MXQ_ERROR_WORKSPACE = 4,         /* workspace missing or smaller than required */
+  MXQ_ERROR_UNSUPPORTED_DEVICE = 5,/* current device is not gfx950 */
+  MXQ_ERROR_LAUNCH = 6             /* the HIP runtime refused a launch */
+} mxq_status;
+
+typedef enum { MXQ_FP8_E4M3 = 0, MXQ_FP8_E5M2 = 1 } mxq_fp8_kind;
+
+typedef enum {
+  MXQ_EPI_NONE = 0,          /* y = acc */
+  MXQ_EPI_BIAS = 1,          /* y = acc + bias[n] */
+  MXQ_EPI_BIAS_GELU_TANH = 2 /* y = GELU_tanh(acc + bias[n]) */
+} mxq_epilogue;
+
+/*
+ * MXFP8 quantizer [P1 "MXFP8和NVFP4技术背景解析"; P5 step 2].
+ *   x      : bf16 [rows, cols], device, read only.
+ *   rows   : > 0.   cols: > 0 and a multiple of 32 (else MXQ_ERROR_UNSUPPORTED_SHAPE).
+ *   kind   : element format, E4M3 or E5M2.
+ *   q      : u8 [rows, cols], device, written.
+ *   scales : u8 [rows, cols/32] E8M0, device, written.
+ * One pass over x; codes and scales are bit-exact to the definition above.
+ */
+mxq_status mxq_quantize_mxfp8(const void* x, int64_t rows, int64_t cols, mxq_fp8_kind kind,
+                              void* q, void* scales, void* stream);
+
+/* Bytes of device workspace mxq_quantize_nvfp4 needs (dynamic mode) for this
+ * shape; 0 for invalid shapes.  The workspace holds per-workgroup partial
+ * maxima; it needs no initialization and its contents are scratch. */
+size_t mxq_quantize_nvfp4_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * NVFP4 quantizer [P1 "MXFP8和NVFP4技术背景解析", step 2 dynamic per-tensor scale;
+ * P2 section 3.1: outputs FP4 data, FP8 scales, FP32 global scale].
+ *   x                : bf16 [rows, cols], device.
+ *   rows, cols       : > 0, cols a multiple of 16.
+ *   global_scale_in  : device fp32 decode scale to use (static mode, must be
+ *                      positive and finite), or NULL for the dynamic scale
+ *                      s_g = RN_fp32(amax(x) / 2688) taken over the whole tensor.
+ *   q                : u8 [rows, cols/2] packed E2M1, device, written.
+ *   scales           : u8 [rows, cols/16] E4M3, device, written.
+ *   global_scale_out : device fp32, written with the s_g used (both modes).
+ *   workspace        : device scratch of mxq_quantize_nvfp4_workspace_size bytes
+ *                      (dynamic mode; may be NULL in static mode).
+ * Dynamic mode makes two passes over x (tensor amax, then encode).  Calls that
+ * share a workspace must be ordered on one stream.
+ */
+mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols,
+                              const float* global_scale_in, void* q, void* scales,
+                              float* global_scale_out, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * MXFP8 block-scaled GEMM [P3: every nn.Linear runs quantized; P2 §5.2: 128 alignment].
+ *   C[m, n] = epi( sum_k val(a_q[m,k]) 2^(a_s[m,k/32]-127) val(w_q[n,k]) 2^(w_s[n,k/32]-127)
+ *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.
+ *   a_q, a_scales : A codes u8 [M, K] and E8M0 [M, K/32] (from mxq_quantize_mxfp8).
+ *   w_q, w_scales : W codes u8 [N, K] and E8M0 [N, K/32].
+ *   a_kind, w_kind: element formats of A and W (E4M3 / E5M2, may differ).
+ *   M, N, K       : > 0, multiples of 128 (else MXQ_ERROR_UNSUPPORTED_SHAPE).
+ *   bias          : bf16 [N] device (required unless epi == MXQ_EPI_NONE).
+ *   c             : bf16 [M, N] device, written.
+ */
+mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_kind,
+                          const void* w_q, const void* w_scales, mxq_fp8_kind w_kind,
+                          int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi,
+                          void* c, void* stream);
+
+/*
+ * NVFP4 block-scaled GEMM [P1 NVFP4 paragraph; P2 §3.1].
+ *   C[m, n] = epi( s_ga s_gw sum_k val(a_q) val(a_s[m,k/16]) val(w_q) val(w_s[n,k/16])
+ *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.
+ *   a_q, a_scales, a_global : packed E2M1 [M, K/2], E4M3 [M, K/16], device fp32 s_ga.
+ *   w_q, w_scales, w_global : packed E2M1 [N, K/2], E4M3 [N, K/16], device fp32 s_gw.
+ *   M, N, K, bias, epi, c   : as mxq_gemm_mxfp8.
+ */
+mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_global,
+                          const void* w_q, const void* w_scales, const float* w_global,
+                          int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi,
+                          void* c, void* stream);
+
+/* Static text for a status code. */
+const char* mxq_status_string(mxq_status s);
+
+/* Detail of the last non-success status returned on this thread ("" if none). */
+const char* mxq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H_ */

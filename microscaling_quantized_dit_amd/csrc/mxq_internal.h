@@ -1,0 +1,78 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// Host-side launchers (each returns the hipError_t of its launch).
+hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void* q, void* scales,
+                                 hipStream_t stream);
+
+// Workgroups (= partial maxima) the NVFP4 amax pass uses for n_elems.
+int nvfp4_amax_partials(int64_t n_elems);
+hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* global_in, void* q,
+                                 void* scales, float* global_out, uint32_t* partials,
+                                 hipStream_t stream);
+
+hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q,
+                             const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
+                             const void* bias, int epi, void* c, hipStream_t stream);
+
+hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q,
+                             const void* w_s, const float* w_g, int64_t M, int64_t N, int64_t K,
+                             const void* bias, int epi, void* c, hipStream_t stream);
+
+}  // namespace mxq
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+namespace mxq {
+namespace dev {
+
+// bf16 bit pattern (low/high half of a dword) widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Max of the 15-bit magnitudes of the eight bf16 values in a uint4, as a
+// packed pair (the caller folds the halves).  Integer order of bf16 magnitude
+// bits is the order of the magnitudes for finite values.
+__device__ __forceinline__ uint32_t mag_max_pk(uint4 v) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  const uint32_t m = 0x7FFF7FFFu;
+  us2 a = __builtin_bit_cast(us2, v.x & m), b = __builtin_bit_cast(us2, v.y & m);
+  us2 c = __builtin_bit_cast(us2, v.z & m), d = __builtin_bit_cast(us2, v.w & m);
+  us2 ab = __builtin_elementwise_max(a, b), cd = __builtin_elementwise_max(c, d);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(ab, cd));
+}
+
+__device__ __forceinline__ uint32_t fold_halves_max(uint32_t pk) {
+  uint32_t lo = pk & 0xFFFFu, hi = pk >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// Round an fp32 to bf16 (nearest, ties to even); inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// GELU, tanh form: 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
+__device__ __forceinline__ float gelu_tanh(float y) {
+  const float k0 = 0.7978845608028654f;
+  const float k1 = 0.044715f;
+  return 0.5f * y * (1.0f + tanhf(k0 * (y + k1 * y * y * y)));
+}
+
+// Remap a linear workgroup id so that ids placed round-robin on the 8 XCDs
+// become contiguous ranges per XCD (neighbouring tiles share one L2).
+__device__ __forceinline__ int xcd_remap(int wg, int n_wg) {
+  const int n_xcd = 8;
+  int per = n_wg / n_xcd;
+  if (wg >= per * n_xcd) return wg;
+  return (wg % n_xcd) * per + wg / n_xcd;
+}
+
+}  // namespace dev
+}  // namespace mxq
+#endif

@@ -1,0 +1,120 @@
+// MXFP8 quantizer for gfx950: bf16 -> E4M3/E5M2 codes + one E8M0 scale per 32
+// values along a row.
+//
+// Definition (page "NVIDIA量化推理：5步极速优化显存+成功率翻倍", section
+// "MXFP8和NVFP4技术背景解析": MXFP8 = OCP 8-bit microscaling, blocks of 32 sharing
+// one scale; page "FP8量化技术提升SD3.5…", step 2: q = round(x / scale)):
+//   E = floor(log2 amax_block) - emax (8 for E4M3, 15 for E5M2), clamped to
+//   [-127, 127], -127 for an all-zero block; scale byte E + 127;
+//   q = RNE_sat(x / 2^E), sign bit copied from x.
+//
+// HBM-bound, one pass.  The tensor is treated as a flat stream (cols % 32 == 0,
+// so blocks never straddle rows and the scale of element e is scales[e / 32]).
+// Each lane takes 8 consecutive values (one 16-byte load), four neighbouring
+// lanes form a 32-block and find its amax with two cross-lane max steps.
+// x / 2^E is exact in fp32 (2^-E is a normal fp32 for every reachable E), and
+// the hardware fp8 conversion rounds to nearest even; it turns magnitudes at or
+// above the saturation midpoint into NaN, so inputs are clamped to the largest
+// finite value first (clamping an exactly scaled value never changes an RNE
+// result below the clamp and yields the saturated code above it).
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte chunks per lane, kept in flight together
+
+template <int KIND>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<0> {  // E4M3 ("fn"): largest finite 448 = 1.75 * 2^8
+  static constexpr int emax = 8;
+  static constexpr float maxval = 448.0f;
+  template <bool HI>
+  static __device__ __forceinline__ int cvt(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+  }
+};
+template <>
+struct Fp8Traits<1> {  // E5M2: largest finite 57344 = 1.75 * 2^15
+  static constexpr int emax = 15;
+  static constexpr float maxval = 57344.0f;
+  template <bool HI>
+  static __device__ __forceinline__ int cvt(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+  }
+};
+
+// Shared exponent E from the block's largest bf16 magnitude bits.
+template <int KIND>
+__device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  uint32_t ef = amax_bits >> 7;
+  int fl = ef ? (int)ef - 127                          // normal: exponent field
+              : (31 - __clz((int)amax_bits)) - 133;    // subnormal: mant * 2^-133
+  int e = fl - Fp8Traits<KIND>::emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <int KIND>
+__device__ __forceinline__ int encode4(uint32_t w0, uint32_t w1, float inv) {
+  using T = Fp8Traits<KIND>;
+  const float hi = T::maxval, lo = -T::maxval;
+  float f0 = __builtin_amdgcn_fmed3f(dev::bf16_lo(w0) * inv, lo, hi);
+  float f1 = __builtin_amdgcn_fmed3f(dev::bf16_hi(w0) * inv, lo, hi);
+  float f2 = __builtin_amdgcn_fmed3f(dev::bf16_lo(w1) * inv, lo, hi);
+  float f3 = __builtin_amdgcn_fmed3f(dev::bf16_hi(w1) * inv, lo, hi);
+  int r = T::template cvt<false>(f0, f1, 0);
+  return T::template cvt<true>(f2, f3, r);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restrict__ x, int64_t n_chunks,
+                                                          uint2* __restrict__ q, uint8_t* __restrict__ s) {
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll);
+  uint4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    int64_t c = base + u * kThreads + t;
+    v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + u * kThreads + t;
+    // Lanes 4j..4j+3 hold chunks 4j'..4j'+3 of one 32-block (n_chunks % 4 == 0,
+    // so a group is entirely in or entirely out of range).
+    uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    const int E = block_exponent<KIND>(m);
+    const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, normal
+    uint2 out;
+    out.x = (uint32_t)encode4<KIND>(v[u].x, v[u].y, inv);
+    out.y = (uint32_t)encode4<KIND>(v[u].z, v[u].w, inv);
+    if (c < n_chunks) {
+      q[c] = out;
+      if ((t & 3) == 0) s[c >> 2] = (uint8_t)(E + 127);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void* q, void* scales,
+                                 hipStream_t stream) {
+  const int64_t n_chunks = n_elems / 8;
+  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (kind == 0)
+    hipLaunchKernelGGL(k_quant_mxfp8<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const uint4*)x, n_chunks, (uint2*)q, (uint8_t*)scales);
+  else
+    hipLaunchKernelGGL(k_quant_mxfp8<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       (const uint4*)x, n_chunks, (uint2*)q, (uint8_t*)scales);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

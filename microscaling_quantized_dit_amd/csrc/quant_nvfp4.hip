@@ -1,0 +1,241 @@
+// NVFP4 quantizer for gfx950: bf16 -> packed E2M1 codes, one E4M3 scale per 16
+// values along a row, and an fp32 per-tensor decode scale.
+//
+// Definition (page "NVIDIA量化推理：5步极速优化显存+成功率翻倍", NVFP4 paragraph:
+// E2M1 in blocks of 16 with FP8 scales; step 2: dynamic per-tensor scale;
+// page "NVIDIA Blackwell平台FP4量化技术解析与图像生成优化", section 3.1: the runtime
+// quantizer outputs FP4 data, FP8 block scales and an FP32 global scale):
+//   s_g = RN_fp32(amax_tensor / 2688)   (1 for an all-zero tensor; or given)
+//   S_b = RN_E4M3_sat(amax_block / (6 s_g))
+//   q   = RN_E2M1_sat(x / (S_b s_g))    (magnitude 0 when S_b = 0), sign copied.
+//
+// Dynamic mode is two passes: k_amax_partials writes one maximum per workgroup
+// (no zero-initialised state, no atomics), k_quant_nvfp4 folds those and encodes.
+//
+// Exact rounding at HBM speed.  Both quotients above are inexact in fp32, so
+// each is evaluated twice, with the divisor's reciprocal nudged down and up by
+// 2^-19 (far more than the <= ~2^-21.5 total relative error of the fp32
+// reciprocal and products).  The two results bracket the exact quotient; if
+// the hardware round-to-nearest conversion gives the same code for both ends,
+// no rounding midpoint lies between them and that code is the exact answer.
+// Otherwise (an exact tie or a near tie, or a reciprocal outside the fp32
+// normal range) the decision is redone with exact fp64 comparisons: every
+// threshold (midpoint x S_b x s_g, or midpoint x 6 x s_g) has at most
+// 5 + 4 + 24 significant bits and is exact in fp64.
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kAmaxThreads = 1024;
+constexpr int kMaxPartials = 256;
+
+__device__ __forceinline__ uint32_t max_pk_u16(uint32_t a, uint32_t b) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a),
+                                                                __builtin_bit_cast(us2, b)));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  return m;
+}
+
+// Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __restrict__ x, int64_t n_chunks,
+                                                                uint32_t* __restrict__ partials) {
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  uint32_t pk = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  for (; c + 3 * stride < n_chunks; c += 4 * stride) {
+    uint4 a = x[c], b = x[c + stride], d = x[c + 2 * stride], e = x[c + 3 * stride];
+    pk = max_pk_u16(pk, max_pk_u16(max_pk_u16(dev::mag_max_pk(a), dev::mag_max_pk(b)),
+                                   max_pk_u16(dev::mag_max_pk(d), dev::mag_max_pk(e))));
+  }
+  for (; c < n_chunks; c += stride) pk = max_pk_u16(pk, dev::mag_max_pk(x[c]));
+  uint32_t m = wave_max(dev::fold_halves_max(pk));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int i = 0; i < kAmaxThreads / 64; ++i) r = max(r, red[i]);
+    partials[blockIdx.x] = r;
+  }
+}
+
+// E4M3 value of a magnitude code 0..126: subnormal m * 2^-9, normal (8+m) 2^(e-10).
+__device__ __forceinline__ double e4m3_value(int c) {
+  int e = c >> 3, m = c & 7;
+  return e == 0 ? (double)m * 0x1p-9 : ldexp((double)(8 + m), e - 10);
+}
+
+// Exact S_b code: the E4M3 code nearest to amax / (6 s_g), ties to the even code,
+// saturating at 448 (code 126).  Binary search on exact fp64 comparisons.
+__device__ __noinline__ int exact_block_scale(double amax, double six_sg) {
+  if (amax >= 448.0 * six_sg) return 126;
+  int lo = 0, hi = 126;                  // invariant: val(lo) * d <= amax < val(hi) * d
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (e4m3_value(mid) * six_sg <= amax) lo = mid; else hi = mid;
+  }
+  double t = 0.5 * (e4m3_value(lo) + e4m3_value(hi)) * six_sg;
+  if (amax < t) return lo;
+  if (amax > t) return hi;
+  return (lo & 1) ? hi : lo;
+}
+
+// Exact E2M1 magnitude code of |x| / D (D = S_b s_g exact in fp64): count the
+// rounding midpoints passed; at a tie the even code wins, so the midpoints
+// between (0, 0.5), (1, 1.5), (2, 3), (4, 6) need a strict '>' and the others '>='.
+__device__ __noinline__ uint32_t exact_e2m1(double ax, double D) {
+  uint32_t c = 0;
+  c += ax > 0.25 * D;
+  c += ax >= 0.75 * D;
+  c += ax > 1.25 * D;
+  c += ax >= 1.75 * D;
+  c += ax > 2.5 * D;
+  c += ax >= 3.5 * D;
+  c += ax > 5.0 * D;
+  return c;
+}
+
+// Eight bf16 values (one uint4) -> eight E2M1 codes (a dword, element 2j in the low
+// nibble of byte j), using reciprocal r of the divisor (0 encodes +-0).
+__device__ __forceinline__ uint32_t encode8(uint4 v, float r) {
+  uint32_t out = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, dev::bf16_lo(v.x) * r, dev::bf16_hi(v.x) * r, 1.0f, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, dev::bf16_lo(v.y) * r, dev::bf16_hi(v.y) * r, 1.0f, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, dev::bf16_lo(v.z) * r, dev::bf16_hi(v.z) * r, 1.0f, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, dev::bf16_lo(v.w) * r, dev::bf16_hi(v.w) * r, 1.0f, 3);
+  return out;
+}
+
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restrict__ x, int64_t n_chunks,
+                                                          const float* __restrict__ global_in,
+                                                          const uint32_t* __restrict__ partials, int n_partials,
+                                                          uint32_t* __restrict__ q, uint8_t* __restrict__ s,
+                                                          float* __restrict__ global_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll);
+  uint4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    int64_t c = base + u * kThreads + t;
+    v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- the global decode scale s_g
+  float sg;
+  if (global_in) {
+    sg = *global_in;
+  } else {
+    uint32_t m = t < n_partials ? partials[t] : 0u;
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    // IEEE (correctly rounded) fp32 division: RN_fp32(amax / 2688).
+    sg = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 2688.0f;
+  }
+  if (blockIdx.x == 0 && t == 0) *global_out = sg;
+
+  // ---- per-kernel constants: bracketing reciprocals of 6 s_g
+  const double six_sg = 6.0 * (double)sg;                   // exact (3 x 24 bits)
+  const double r6 = 1.0 / six_sg;
+  const float r6_lo = (float)(r6 * (1.0 - 0x1p-19));
+  const float r6_hi = (float)(r6 * (1.0 + 0x1p-19));
+  const bool fast6 = r6 < 0x1p126 && r6 > 0x1p-126;
+
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + u * kThreads + t;
+    // lanes 2j, 2j+1 hold the two halves of one 16-block (n_chunks is even)
+    uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    const float amax_b = __uint_as_float(m << 16);
+
+    // ---- S_b = RN_E4M3(amax_b / (6 s_g))
+    int sb;
+    {
+      float ql = __builtin_amdgcn_fmed3f(amax_b * r6_lo, 0.0f, 448.0f);
+      float qh = __builtin_amdgcn_fmed3f(amax_b * r6_hi, 0.0f, 448.0f);
+      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ql, qh, 0, false);
+      int cl = pk & 0xFF, ch = (pk >> 8) & 0xFF;
+      sb = cl;
+      if (cl != ch || !fast6) sb = exact_block_scale((double)amax_b, six_sg);
+    }
+    const float S = (float)e4m3_value(sb);
+
+    // ---- codes: x / (S s_g), bracketed
+    uint32_t codes;
+    const float D = S * sg;
+    if (S == 0.0f) {
+      codes = encode8(v[u], 0.0f);                           // signed zeros
+    } else {
+      // exact path when the reciprocal would lose range, or when the block scale
+      // saturated (only a static scale can then push quotients far past 6)
+      bool exact = !(D >= 0x1p-126f) || sb == 126;
+      uint32_t lo = 0, hi = 0;
+      if (!exact) {
+        const float r = __builtin_amdgcn_rcpf(D);             // <= 1 ulp
+        lo = encode8(v[u], r * (1.0f - 0x1p-19f));
+        hi = encode8(v[u], r * (1.0f + 0x1p-19f));
+        exact = lo != hi;
+      }
+      codes = lo;
+      if (exact) {
+        const double Dd = (double)S * (double)sg;           // exact (4 x 24 bits)
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        codes = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          double ax = (double)__uint_as_float((bits & 0x7FFFu) << 16);
+          uint32_t nib = exact_e2m1(ax, Dd) | ((bits >> 12) & 0x8u);
+          codes |= nib << (4 * i);
+        }
+      }
+    }
+    if (c < n_chunks) {
+      q[c] = codes;
+      if ((t & 1) == 0) s[c >> 1] = (uint8_t)sb;
+    }
+  }
+}
+
+}  // namespace
+
+int nvfp4_amax_partials(int64_t n_elems) {
+  const int64_t n_chunks = n_elems / 8;
+  int64_t p = (n_chunks + (int64_t)kAmaxThreads * 4 - 1) / ((int64_t)kAmaxThreads * 4);
+  if (p < 1) p = 1;
+  if (p > kMaxPartials) p = kMaxPartials;
+  return (int)p;
+}
+
+hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* global_in, void* q,
+                                 void* scales, float* global_out, uint32_t* partials,
+                                 hipStream_t stream) {
+  const int64_t n_chunks = n_elems / 8;
+  int n_partials = 0;
+  if (!global_in) {
+    n_partials = nvfp4_amax_partials(n_elems);
+    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream,
+                       (const uint4*)x, n_chunks, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x,
+                     n_chunks, global_in, partials, n_partials, (uint32_t*)q, (uint8_t*)scales, global_out);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

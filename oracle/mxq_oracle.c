@@ -123,14 +123,18 @@ static int finite_table(int fmt, double* vals) {
 }
 
 /* Magnitude code of RNE_sat(num / den), num >= 0, den > 0, both exact fp64,
- * for the value table vals[0..n).  Walk the table: find v_i <= q < v_{i+1},
+ * for the value table vals[0..n).  Find v_i <= q < v_{i+1} by bisection,
  * then compare q with the midpoint; a tie goes to the even code.  q at or
  * above the largest value saturates. */
 static int round_in_table(const double* vals, int n, double num, double den) {
     if (!(num >= 0.0) || !(den > 0.0)) orc_fail("round_quotient domain");
     if (num >= exact_mul(vals[n - 1], den)) return n - 1;
-    int i = 0;
-    while (num >= exact_mul(vals[i + 1], den)) ++i;
+    /* bisection keeping vals[i] * den <= num < vals[j] * den (vals[0] = 0) */
+    int i = 0, j = n - 1;
+    while (j - i > 1) {
+        int k = (i + j) / 2;
+        if (num >= exact_mul(vals[k], den)) i = k; else j = k;
+    }
     double mid = 0.5 * (vals[i] + vals[i + 1]);       /* exact: one more bit */
     double mden = exact_mul(mid, den);
     if (num < mden) return i;

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every symbol include/mxq.h declares, and
+rejects invalid calls on the host, before any launch or device query.
+
+No compute call is made here: every call below fails validation (fake but
+aligned pointers are never dereferenced).  The device gate is exercised only
+where no GPU is present.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import microscaling_quantized_dit_amd as mxq
+from tests.conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+FAKE = 0x10000          # aligned, never dereferenced
+FAKE2 = 0x20000
+MIS = 0x10008           # 8 mod 16
+
+SUCCESS, INVALID, SHAPE, MISALIGNED, WORKSPACE, DEVICE, LAUNCH = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mxq.library_path()):
+        import microscaling_quantized_dit_amd.build as b
+        b.build()
+    return mxq.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_quantize_nvfp4_workspace_size",
+              "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_status_string", "mxq_last_error"]:
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    assert sorted(mxq.SYMBOLS) == declared_symbols()
+
+
+def test_status_strings(lib):
+    for code, word in [(SUCCESS, b"success"), (INVALID, b"invalid"), (SHAPE, b"shape"),
+                       (MISALIGNED, b"misaligned"), (WORKSPACE, b"workspace"), (DEVICE, b"device"),
+                       (LAUNCH, b"launch")]:
+        assert word in lib.mxq_status_string(code)
+
+
+def _q8(lib, x=FAKE, rows=4, cols=64, kind=0, q=FAKE, s=FAKE2):
+    return lib.mxq_quantize_mxfp8(x, rows, cols, kind, q, s, None)
+
+
+def test_quantize_mxfp8_validation(lib):
+    assert _q8(lib, x=None) == INVALID
+    assert _q8(lib, q=None) == INVALID
+    assert _q8(lib, rows=0) == INVALID
+    assert _q8(lib, cols=-32) == INVALID
+    assert _q8(lib, kind=2) == INVALID
+    assert _q8(lib, cols=48) == SHAPE
+    assert _q8(lib, rows=1 << 62, cols=64) == SHAPE
+    assert _q8(lib, x=MIS) == MISALIGNED
+    assert _q8(lib, s=MIS) == MISALIGNED
+    assert b"multiple of 32" in (_q8(lib, cols=48) and lib.mxq_last_error())
+
+
+def test_quantize_nvfp4_validation(lib):
+    ws = lib.mxq_quantize_nvfp4_workspace_size
+    assert ws(128, 256) >= 4 and ws(128, 24) == 0 and ws(0, 16) == 0
+    need = ws(4, 64)
+
+    def call(x=FAKE, rows=4, cols=64, gin=None, q=FAKE, s=FAKE2, gout=FAKE, w=FAKE2, wsb=need):
+        return lib.mxq_quantize_nvfp4(x, rows, cols, gin, q, s, gout, w, wsb, None)
+
+    assert call(x=None) == INVALID
+    assert call(gout=None) == INVALID
+    assert call(cols=0) == INVALID
+    assert call(cols=24) == SHAPE
+    assert call(q=MIS) == MISALIGNED
+    assert call(gout=FAKE + 2) == MISALIGNED
+    assert call(w=None) == WORKSPACE
+    assert call(wsb=need - 4) == WORKSPACE
+
+
+def _g8(lib, M=128, N=256, K=256, bias=None, epi=0, c=FAKE, a=FAKE, ak=0, wk=0):
+    return lib.mxq_gemm_mxfp8(a, FAKE2, ak, FAKE, FAKE2, wk, M, N, K, bias, epi, c, None)
+
+
+def test_gemm_mxfp8_validation(lib):
+    assert _g8(lib, a=None) == INVALID
+    assert _g8(lib, c=None) == INVALID
+    assert _g8(lib, M=0) == INVALID
+    assert _g8(lib, epi=3) == INVALID
+    assert _g8(lib, epi=1) == INVALID            # bias required
+    assert _g8(lib, ak=5) == INVALID
+    assert _g8(lib, K=192) == SHAPE               # 128 alignment rule
+    assert _g8(lib, M=200) == SHAPE
+    assert _g8(lib, M=1 << 20, K=1 << 12) == SHAPE  # A would exceed 2 GiB
+    assert _g8(lib, c=MIS) == MISALIGNED
+    assert _g8(lib, epi=2, bias=MIS) == MISALIGNED
+
+
+def test_gemm_nvfp4_validation(lib):
+    def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE):
+        return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, M, N, K, bias, epi, c, None)
+
+    assert call(ag=None) == INVALID
+    assert call(N=100) == SHAPE
+    assert call(epi=2) == INVALID
+    assert call(ag=FAKE + 1) == MISALIGNED
+
+
+@pytest.mark.skipif(gpu_available(), reason="device gate is only observable without a GPU")
+def test_device_gate_without_gpu(lib):
+    """Valid arguments reach the device check, which refuses without a gfx950."""
+    assert _q8(lib) == DEVICE
+    assert _g8(lib) == DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding never falls back to anything when libmxq.so is absent."""
+    import importlib
+    m = importlib.reload(mxq)
+    monkeypatch.setattr(m, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(m, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        m.load()
+    importlib.reload(mxq)

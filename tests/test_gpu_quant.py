@@ -1,0 +1,169 @@
+"""GPU quantizers against the CPU oracle: codes, scales and the global scale must
+be bit-identical (the quantizers have exactly one correct result).
+
+Inputs are seeded (microscaling_quantized_dit_amd.inputs) or crafted bit
+patterns; every expected value is computed by the oracle on the CPU from the
+same input bytes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from microscaling_quantized_dit_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [("e4m3", oracle.E4M3), ("e5m2", oracle.E5M2)]
+
+
+def _dev(bits):
+    return inputs.to_torch(bits, "cuda")
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _check_mx(mxq, bits, kind, fmt, rows=None):
+    q, s = mxq.quantize_mxfp8(_dev(bits), kind)
+    q, s = _np(q), _np(s)
+    if rows is None:
+        rq, rs = oracle.quantize_mxfp8(bits, fmt)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(q, rq)
+    else:
+        rq, rs = oracle.quantize_mxfp8(bits[rows], fmt)
+        np.testing.assert_array_equal(s[rows], rs)
+        np.testing.assert_array_equal(q[rows], rq)
+
+
+def _check_nv(mxq, bits, rows=None, static=None):
+    import torch
+    gin = None if static is None else torch.tensor([static], dtype=torch.float32, device="cuda")
+    q, s, g = mxq.quantize_nvfp4(_dev(bits), global_scale=gin)
+    q, s, g = _np(q), _np(s), float(_np(g)[0])
+    if static is None:
+        rg = oracle.nvfp4_global_scale(bits)
+    else:
+        rg = np.float32(static)
+    assert np.float32(g).tobytes() == np.float32(rg).tobytes()
+    sub = bits if rows is None else bits[rows]
+    rq, rs, _ = oracle.quantize_nvfp4(sub, global_scale=rg)
+    np.testing.assert_array_equal(s if rows is None else s[rows], rs)
+    np.testing.assert_array_equal(q if rows is None else q[rows], rq)
+
+
+# ------------------------------------------------------------- tiny config
+
+@pytest.mark.parametrize("kind,fmt", KINDS)
+def test_mxfp8_tiny(mxq, kind, fmt):
+    _check_mx(mxq, inputs.tiny_activation(), kind, fmt)
+    _check_mx(mxq, inputs.weight(256, 256, std=0.02, stream="tiny/W"), kind, fmt)
+
+
+def test_nvfp4_tiny_dynamic_and_static(mxq):
+    a = inputs.tiny_activation()
+    _check_nv(mxq, a)
+    _check_nv(mxq, inputs.weight(256, 256, std=0.02, stream="tiny/W"))
+    for sg in [1.0, 0.0625, 0.013671875, 3.3e-3]:
+        _check_nv(mxq, a, static=sg)
+
+
+# ------------------------------------------------------ exhaustive bf16 sweep
+
+def _sweep(block: int, amax_bits):
+    """Every finite bf16 pattern, (block - 1) per block, each block completed by
+    one 'controller' value that fixes the block maximum."""
+    pats = np.array([p for p in range(65536) if (p & 0x7F80) != 0x7F80], np.uint16)
+    out = []
+    for a in amax_bits:
+        per = block - 1
+        n = (pats.size + per - 1) // per
+        body = np.resize(pats, n * per).reshape(n, per)
+        ctrl = np.full((n, 1), a, np.uint16)
+        out.append(np.concatenate([ctrl, body], axis=1).reshape(-1))
+    flat = np.concatenate(out)
+    cols = 32 * 64
+    pad = (-flat.size) % cols
+    return np.concatenate([flat, np.zeros(pad, np.uint16)]).reshape(-1, cols)
+
+
+@pytest.mark.parametrize("kind,fmt", KINDS)
+def test_mxfp8_exhaustive_bf16(mxq, kind, fmt):
+    # controllers: the block max ranges over small, typical and huge magnitudes
+    x = _sweep(32, [0x0000, 0x3F80, 0x4B00, 0x7F7F, 0x0001, 0x2000])
+    _check_mx(mxq, x, kind, fmt)
+
+
+def test_nvfp4_exhaustive_bf16(mxq):
+    x = _sweep(16, [0x3F80, 0x4B00, 0x0080])
+    _check_nv(mxq, x)                         # dynamic: s_g from 0x7F7F's neighbours
+    _check_nv(mxq, x, static=1.0)
+    _check_nv(mxq, x, static=2.0 ** -20)
+
+
+# --------------------------------------------------------- crafted edge cases
+
+def test_edge_cases(mxq):
+    z = np.zeros((2, 64), np.uint16)
+    z[0, 3] = 0x8000                                     # -0
+    z[1, 5] = 0x0001                                     # smallest subnormal
+    for kind, fmt in KINDS:
+        _check_mx(mxq, z, kind, fmt)
+    _check_nv(mxq, np.zeros((1, 16), np.uint16))         # all-zero tensor: s_g = 1
+    _check_nv(mxq, z)
+    # exact ties: amax/2688 a power of two, block maxima on E4M3 midpoints, elements on E2M1 midpoints
+    vals = np.array([2688.0 * 4, 6 * 17.0 * 4, 0.25 * 4, 0.75 * 4, 1.25 * 4, 2.5 * 4, 5 * 4, 3.5 * 4,
+                     -1.75 * 4, 448.0 * 6 * 4, 1e-30, -1e-30, 3.0, 6.5 * 4, -5.0 * 4, 0.0], np.float64)
+    row = inputs.bf16_bits(vals)
+    t = np.tile(row, (4, 4))
+    _check_nv(mxq, t)
+    _check_nv(mxq, t, static=4.0)
+    _check_nv(mxq, t, static=1.0)
+    for kind, fmt in KINDS:
+        _check_mx(mxq, t.reshape(-1, 32), kind, fmt)
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 96), (5, 160), (7, 4128)])
+def test_ragged_shapes(mxq, shape):
+    x = inputs.flux_activation(*shape, seed=5, stream="ragged")
+    for kind, fmt in KINDS:
+        _check_mx(mxq, x, kind, fmt)
+    _check_nv(mxq, x)
+
+
+def test_nvfp4_extreme_tensor_scales(mxq):
+    """Tensors whose amax makes s_g an fp32 subnormal, or 6 s_g's reciprocal leave
+    fp32's normal range, or that span the whole bf16 range."""
+    tiny = np.array([[0x0001, 0x8003, 0x0040, 0x007F, 0x0010, 0x8000, 0x0002, 0x0005] * 4], np.uint16)
+    _check_nv(mxq, tiny)                              # amax ~ 2^-127: s_g subnormal
+    wide = np.array([[0x7F7F, 0x0001, 0x3F80, 0xBF80, 0x0080, 0x4000, 0x8001, 0x7F00] * 4], np.uint16)
+    _check_nv(mxq, wide)
+    _check_nv(mxq, wide, static=2.0 ** -125)
+    _check_nv(mxq, tiny, static=2.0 ** 100)
+
+
+# -------------------------------------------------- full-size (config 2 shapes)
+
+@pytest.mark.parametrize("cols", [3072, 12288])
+def test_flux_activation_full_size(mxq, cols):
+    """The 4608-token FLUX activations at their real shapes: MXFP8 checked in
+    full, NVFP4 on every 7th row plus the exact global scale."""
+    x = inputs.flux_activation(4608, cols, seed=0, stream="cfg2/x%d" % cols)
+    _check_mx(mxq, x, "e4m3", oracle.E4M3)
+    rows = np.arange(0, 4608, 7)
+    _check_mx(mxq, x, "e5m2", oracle.E5M2, rows=rows)
+    _check_nv(mxq, x, rows=rows)
+
+
+def test_deterministic(mxq):
+    import torch
+    x = _dev(inputs.flux_activation(512, 3072, seed=9, stream="det"))
+    a = [t.clone() for t in mxq.quantize_nvfp4(x)]
+    b = mxq.quantize_nvfp4(x)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    a = [t.clone() for t in mxq.quantize_mxfp8(x)]
+    b = mxq.quantize_mxfp8(x)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
