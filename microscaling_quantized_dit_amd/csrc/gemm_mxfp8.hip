@@ -30,36 +30,27 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;        // rows of W (n) and of A (m) per workgroup
-constexpr int kBK = 128;          // K bytes per stage
-constexpr int kRow = kBK + 16;    // padded LDS row (bytes)
-constexpr int kStage = 2 * kTile * kRow;
+constexpr int kBK = 128;          // K bytes per stage = one LDS row
+constexpr int kOperand = kTile * kBK;          // 32 KiB
+constexpr int kStage = 2 * kOperand;           // W then A
 constexpr int kGroupM = 4;
 
-// One 64-K step of the wave's 128 x 128 tile: 4 W fragments, 4 A fragments,
-// 16 scaled MFMAs.  S selects the 64-K half of the 128-byte stage; the scale
-// dwords were pre-shifted so that byte 2S holds this lane's block.
-template <int AK, int WK, int S>
-__device__ __forceinline__ void substep(v16f (&acc)[4][4], const uint8_t* wl, const uint8_t* al, int g,
-                                        const uint32_t (&scw)[4], const uint32_t (&sca)[4]) {
-  v8i wf[4], af[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* p = wl + 32 * i * kRow;
-    uint4 lo = *(const uint4*)(p + (4 * S + g) * 16), hi = *(const uint4*)(p + (4 * S + 2 + g) * 16);
-    wf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    const uint8_t* q = al + 32 * i * kRow;
-    uint4 lo2 = *(const uint4*)(q + (4 * S + g) * 16), hi2 = *(const uint4*)(q + (4 * S + 2 + g) * 16);
-    af[i] = v8i{(int)lo2.x, (int)lo2.y, (int)lo2.z, (int)lo2.w, (int)hi2.x, (int)hi2.y, (int)hi2.z, (int)hi2.w};
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[i], af[j], acc[i][j], WK, AK, 2 * S,
-                                                                 (int)scw[i], 2 * S, (int)sca[j]);
+// XOR swizzle of the eight 16-byte chunks of an LDS row: row R keeps logical
+// chunk c at physical chunk c ^ swz(R).  The 16 rows read by one quarter-wave
+// (ds_read_b128 is served 16 lanes at a time) then cover all 64 banks.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Fragment of the 32x32x64 operand for this lane: row R of the stage, the two
+// 16-byte chunks c and c + 2 of 64-K half S (lane group g picks c = 4S + g).
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int R, int x, int S, int g) {
+  const uint8_t* p = tile + R * kBK;
+  uint4 lo = *(const uint4*)(p + (((4 * S + g) ^ x) << 4));
+  uint4 hi = *(const uint4*)(p + (((4 * S + 2 + g) ^ x) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
 template <int AK, int WK, int EPI>
@@ -67,7 +58,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N,
     int K) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  // Two stage buffers (codes, then the stage's scale dwords) as distinct objects:
+  // alias analysis can then tell the DMA into one from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(16))) uint32_t sc0[2 * kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t sc1[2 * kTile];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
   const int wg = dev::xcd_remap(blockIdx.x, gridDim.x);
@@ -78,7 +74,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const int tn = (wg % per_group) / gsize;
   const int m0 = tm * kTile, n0 = tn * kTile;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (an SGPR)
   const int wn = wave & 1, wm = wave >> 1;
   const int r = lane & 31, g = lane >> 5;
   const int KB = K / 32;            // scale bytes per row
@@ -89,32 +86,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * K, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KB, 0x00020000);
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc((void*)as_, (short)0, M * KB, 0x00020000);
-  // staging: thread t copies 16-byte chunk (t & 7) of rows (t >> 3) + 32 i, i = 0..7
-  const int voff = (t >> 3) * K + (t & 7) * 16;
-  const int loff = (t >> 3) * kRow + (t & 7) * 16;
-  const int vsw = (wn * 128 + r) * KB, vsa = (wm * 128 + r) * KB;
 
-  uint4 stw[8], sta[8];
-  uint32_t scw[4], sca[4], nscw[4], nsca[4];
-  auto load_stage = [&](int k0) {
+  // Global -> LDS without registers: each buffer_load ... lds moves 1 KiB per wave
+  // (lane i -> LDS bytes [16i, 16i+16) after M0) = 8 rows of 128 B.  Wave w fills
+  // rows [64w, 64w+64) of each operand in 8 loads; lane i takes row (i / 8) of the
+  // load and the global chunk that lands at physical chunk i % 8.  Rows 8j + i/8
+  // have swz = ((i/8) >> 1) + 4 (j & 1), hence two lane offsets.  The stage's scale
+  // dwords (4 MX blocks of every row) follow with one 4-byte-per-lane load per
+  // operand: lane i of wave w -> row 64w + i.
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  const int cx = lchunk ^ (lrow >> 1);
+  const int voff0 = lrow * K + cx * 16, voff1 = lrow * K + (cx ^ 4) * 16;
+  const int vsc = lane * KB;
+  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int k0) {
+    uint8_t* base = buf + wave * 64 * kBK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      stw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, (n0 + 32 * i) * K + k0, 0));
-      sta[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff, (m0 + 32 * i) * K + k0, 0));
+    for (int j = 0; j < 8; ++j) {
+      const int vo = (j & 1) ? voff1 : voff0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 8 * kBK), 16, vo,
+                                               (n0 + wave * 64 + 8 * j) * K + k0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 8 * kBK), 16, vo,
+                                               (m0 + wave * 64 + 8 * j) * K + k0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      nscw[i] = __builtin_amdgcn_raw_buffer_load_b32(rsw, vsw, (n0 + 32 * i) * KB + k0 / 32, 0);
-      nsca[i] = __builtin_amdgcn_raw_buffer_load_b32(rsa, vsa, (m0 + 32 * i) * KB + k0 / 32, 0);
-    }
-  };
-  auto store_stage = [&](int st) {
-    uint8_t* base = lds + st * kStage + loff;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *(uint4*)(base + 32 * i * kRow) = stw[i];
-      *(uint4*)(base + kTile * kRow + 32 * i * kRow) = sta[i];
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + wave * 64), 4, vsc,
+                                             (n0 + wave * 64) * KB + k0 / 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc,
+                                             (m0 + wave * 64) * KB + k0 / 32, 0, 0);
   };
 
   v16f acc[4][4];
@@ -126,26 +123,95 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = K / kBK;
-  load_stage(0);
-  store_stage(0);
+  const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
+  const int wrow = wn * 128 + r, arow = wm * 128 + r;
+  v8i f0w[4], f0a[4], f1w[4], f1a[4];   // fragments of the first / second 64-K half
+  uint32_t scw[4], sca[4], nscw[4], nsca[4];
+  // scale dwords of this lane's rows, shifted so byte 0 / byte 2 hold its block
+  auto read_scales = [&](const uint32_t* sc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nscw[i] = sc[wrow + 32 * i];
+      nsca[i] = sc[kTile + arow + 32 * i];
+    }
+  };
+
+  // Prologue: stages 0 and 1 in flight; wait; stage 0's scales and first-half fragments.
+  dma_stage(lds0, sc0, 0);
+  dma_stage(lds1, sc1, kBK);        // nk == 1: reads past K, never used
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_scales(sc0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f0w[i] = frag(lds0, wrow + 32 * i, x, 0, g);
+    f0a[i] = frag(lds0 + kOperand, arow + 32 * i, x, 0, g);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
-  __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) load_stage((kt + 1) * kBK);
-    const uint8_t* wl = lds + st * kStage + (wn * 128 + r) * kRow;
-    const uint8_t* al = lds + st * kStage + kTile * kRow + (wm * 128 + r) * kRow;
-    substep<AK, WK, 0>(acc, wl, al, g, scw, sca);
-    substep<AK, WK, 1>(acc, wl, al, g, scw, sca);
-    if (kt + 1 < nk) {
-      store_stage(st ^ 1);
+  // Steady state, per stage k (buffer cur = k even ? lds0 : lds1):
+  //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of stage k
+  //   B: wait for stage k+1's DMA and this wave's reads, barrier (cur is now free in
+  //      every wave, stage k+1 visible in nxt)
+  //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of stage k+1; DMA of
+  //      stage k+2 into cur.
+  // Stages past the last are fetched from past K (next row, or zeros past the buffer
+  // end) and never used.
+  auto stage = [&](uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int kt) {
+    // ---- A
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
+    for (int i = 0; i < 4; ++i) {
+      f1w[i] = frag(cur, wrow + 32 * i, x, 1, g);
+      f1a[i] = frag(cur + kOperand, arow + 32 * i, x, 1, g);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f0w[i], f0a[j], acc[i][j], WK, AK, 0,
+                                                                   (int)scw[i], 0, (int)sca[j]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- B
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
+    // ---- C
+    read_scales(snxt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f0w[i] = frag(nxt, wrow + 32 * i, x, 0, g);
+      f0a[i] = frag(nxt + kOperand, arow + 32 * i, x, 0, g);
+    }
+    dma_stage(cur, scur, (kt + 2) * kBK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f1w[i], f1a[j], acc[i][j], WK, AK, 2,
+                                                                   (int)scw[i], 2, (int)sca[j]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // scale reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (i < 9) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // 2 LDS-DMA loads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    stage(lds0, lds1, sc0, sc1, kt);
+    stage(lds1, lds0, sc1, sc0, kt + 1);
   }
+  if (kt < nk) stage(lds0, lds1, sc0, sc1, kt);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA outlives the workgroup
 
   // ---- epilogue: epi(acc) -> bf16, four consecutive n per store
 #pragma unroll
@@ -172,8 +238,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
           for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
         }
         uint2 o;
-        o.x = dev::f32_to_bf16_rne(y[0]) | (dev::f32_to_bf16_rne(y[1]) << 16);
-        o.y = dev::f32_to_bf16_rne(y[2]) | (dev::f32_to_bf16_rne(y[3]) << 16);
+        o.x = dev::pack_bf16x2(y[0], y[1]);
+        o.y = dev::pack_bf16x2(y[2], y[3]);
         *(uint2*)(crow + n) = o;
       }
     }

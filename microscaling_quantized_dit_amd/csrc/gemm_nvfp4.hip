@@ -211,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
           for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
         }
         uint2 o;
-        o.x = dev::f32_to_bf16_rne(y[0]) | (dev::f32_to_bf16_rne(y[1]) << 16);
-        o.y = dev::f32_to_bf16_rne(y[2]) | (dev::f32_to_bf16_rne(y[3]) << 16);
+        o.x = dev::pack_bf16x2(y[0], y[1]);
+        o.y = dev::pack_bf16x2(y[2], y[3]);
         *(uint2*)(crow + n) = o;
       }
     }

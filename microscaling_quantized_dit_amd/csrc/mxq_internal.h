@@ -51,10 +51,11 @@ __device__ __forceinline__ uint32_t fold_halves_max(uint32_t pk) {
   return lo > hi ? lo : hi;
 }
 
-// Round an fp32 to bf16 (nearest, ties to even); inputs are finite.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two fp32 -> two bf16 (nearest, ties to even) packed low|high: v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  v2bf r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // GELU, tanh form: 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
