@@ -17,12 +17,15 @@
 // W is fed as the first operand and A as the second, so each lane ends up with
 // four consecutive output columns n of one output row m: 8-byte bf16 stores.
 //
-// Tiling: 256 (n) x 256 (m) per workgroup, 4 waves in 2 x 2, 128 x 128 per wave
-// (4 x 4 MFMA tiles), K step 128 bytes, two LDS stages (rows padded to 144 B so
-// the 32 rows read by one instruction spread over all banks), next stage loaded
-// into registers while the current one is multiplied.  Workgroup ids are
-// remapped so that tiles sharing operands land on one XCD (one L2), in groups of
-// four M-tiles.
+// Tiling: 256 (n) x 256 (m) output tiles, 4 waves in 2 x 2, 128 x 128 per wave
+// (4 x 4 MFMA tiles), K stages of 128 bytes.  Operands and their scale dwords go
+// from global memory straight into LDS (buffer_load ... lds), two stage buffers,
+// XOR-swizzled rows.  Each stage is split at a mid-stage barrier so that one
+// half's MFMAs overlap the other half's fragment reads and the DMA two stages
+// ahead.  The kernel is persistent (one workgroup per CU): a workgroup walks its
+// tiles as one stream of stages, so the next tile's first stages are in flight
+// during the previous tile's epilogue.  Tiles are ordered so that each XCD (one
+// L2) works on a contiguous range, in groups of four M-tiles.
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -33,7 +36,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
-constexpr int kTile = 256;        // rows of W (n) and of A (m) per workgroup
+constexpr int kTile = 256;        // rows of W (n) and of A (m) per tile
 constexpr int kBK = 128;          // K bytes per stage = one LDS row
 constexpr int kOperand = kTile * kBK;          // 32 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
@@ -66,13 +69,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   __shared__ __attribute__((aligned(16))) uint32_t sc1[2 * kTile];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
-  const int wg = dev::xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (wg / per_group) * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (wg % per_group) % gsize;
-  const int tn = (wg % per_group) / gsize;
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int n_tiles = tiles_m * tiles_n;
+  const int nk = K / kBK;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  // origin of this workgroup's ti-th tile
+  auto origin = [&](int ti, int& m0, int& n0) {
+    const int v = blockIdx.x + ti * gridDim.x;
+    const int wg = dev::xcd_remap(v, n_tiles);
+    const int per_group = kGroupM * tiles_n;
+    const int first_m = (wg / per_group) * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    m0 = (first_m + (wg % per_group) % gsize) * kTile;
+    n0 = ((wg % per_group) / gsize) * kTile;
+  };
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (an SGPR)
@@ -80,8 +89,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const int r = lane & 31, g = lane >> 5;
   const int KB = K / 32;            // scale bytes per row
 
-  // Buffer resources: 32-bit offsets (operands are < 2 GiB, checked by the host),
-  // reads past the end return 0 (rows past M or N are never stored).
+  // Buffer resources with 32-bit offsets (operands are < 2 GiB, checked by the host).
   const auto rw = __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, N * K, 0x00020000);
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * K, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KB, 0x00020000);
@@ -98,36 +106,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const int cx = lchunk ^ (lrow >> 1);
   const int voff0 = lrow * K + cx * 16, voff1 = lrow * K + (cx ^ 4) * 16;
   const int vsc = lane * KB;
-  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int k0) {
+  // Every load stays inside its operand.  A wave's 64 rows lie wholly inside or
+  // wholly past M (N), both being multiples of 128; rows past the end, and the
+  // stages after the workgroup's last tile (valid == false), read rows [0, 64)
+  // instead: their products only reach outputs that are never stored.
+  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
     uint8_t* base = buf + wave * 64 * kBK;
+    const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
+    const bool vw = valid && rw0 < N, va = valid && ra0 < M;
+    const int off_w = vw ? rw0 * K + k0 : 0, off_a = va ? ra0 * K + k0 : 0;
+    const int off_sw = vw ? rw0 * KB + k0 / 32 : 0, off_sa = va ? ra0 * KB + k0 / 32 : 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int vo = (j & 1) ? voff1 : voff0;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 8 * kBK), 16, vo,
-                                               (n0 + wave * 64 + 8 * j) * K + k0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 8 * kBK), 16, vo, off_w + j * 8 * K, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 8 * kBK), 16, vo,
-                                               (m0 + wave * 64 + 8 * j) * K + k0, 0, 0);
+                                               off_a + j * 8 * K, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + wave * 64), 4, vsc,
-                                             (n0 + wave * 64) * KB + k0 / 32, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc,
-                                             (m0 + wave * 64) * KB + k0 / 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + wave * 64), 4, vsc, off_sw, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc, off_sa, 0, 0);
   };
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int nk = K / kBK;
   const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
   const int wrow = wn * 128 + r, arow = wm * 128 + r;
   v8i f0w[4], f0a[4], f1w[4], f1a[4];   // fragments of the first / second 64-K half
   uint32_t scw[4], sca[4], nscw[4], nsca[4];
-  // scale dwords of this lane's rows, shifted so byte 0 / byte 2 hold its block
+  // scale dwords of this lane's rows (shifted later so byte 0 / byte 2 hold its block)
   auto read_scales = [&](const uint32_t* sc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -136,29 +140,49 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     }
   };
 
-  // Prologue: stages 0 and 1 in flight; wait; stage 0's scales and first-half fragments.
-  dma_stage(lds0, sc0, 0);
-  dma_stage(lds1, sc1, kBK);        // nk == 1: reads past K, never used
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  read_scales(sc0);
+  // epi(acc) -> bf16 for the tile at (m0, n0), four consecutive n per 8-byte store.
+  auto epilogue = [&](const v16f (&acc)[4][4], int m0, int n0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f0w[i] = frag(lds0, wrow + 32 * i, x, 0, g);
-    f0a[i] = frag(lds0 + kOperand, arow + 32 * i, x, 0, g);
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 128 + 32 * j + r;
+      uint16_t* crow = c + (size_t)m * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
+      for (int i = 0; i < 4; ++i) {
+        // M, N are multiples of 128: whole 32-row / 32-column MFMA tiles are in or out
+        if (m0 + wm * 128 + 32 * j < M && n0 + wn * 128 + 32 * i < N) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
+            float y[4] = {acc[i][j][4 * qd], acc[i][j][4 * qd + 1], acc[i][j][4 * qd + 2], acc[i][j][4 * qd + 3]};
+            if (EPI >= 1) {
+              uint2 b = *(const uint2*)(bias + n);
+              y[0] += dev::bf16_lo(b.x);
+              y[1] += dev::bf16_hi(b.x);
+              y[2] += dev::bf16_lo(b.y);
+              y[3] += dev::bf16_hi(b.y);
+            }
+            if (EPI == 2) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
+            }
+            uint2 o;
+            o.x = dev::pack_bf16x2(y[0], y[1]);
+            o.y = dev::pack_bf16x2(y[2], y[3]);
+            *(uint2*)(crow + n) = o;
+          }
+        }
+      }
+    }
+  };
 
-  // Steady state, per stage k (buffer cur = k even ? lds0 : lds1):
-  //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of stage k
-  //   B: wait for stage k+1's DMA and this wave's reads, barrier (cur is now free in
-  //      every wave, stage k+1 visible in nxt)
-  //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of stage k+1; DMA of
-  //      stage k+2 into cur.
-  // Stages past the last are fetched from past K (next row, or zeros past the buffer
-  // end) and never used.
-  auto stage = [&](uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int kt) {
+  // One stage (buffer cur holds it; nxt holds the next one, possibly of the next tile):
+  //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of this stage
+  //   B: wait for the next stage's DMA and this wave's reads, barrier (cur is now
+  //      free in every wave, the next stage visible in nxt)
+  //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of the next stage;
+  //      DMA of the stage after next (given by dm0, dn0, dk0, dvalid) into cur.
+  auto stage = [&](v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int dm0,
+                   int dn0, int dk0, bool dvalid) {
     // ---- A
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -187,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       f0w[i] = frag(nxt, wrow + 32 * i, x, 0, g);
       f0a[i] = frag(nxt + kOperand, arow + 32 * i, x, 0, g);
     }
-    dma_stage(cur, scur, (kt + 2) * kBK);
+    dma_stage(cur, scur, dm0, dn0, dk0, dvalid);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -205,52 +229,72 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
 #pragma unroll
     for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
   };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    stage(lds0, lds1, sc0, sc1, kt);
-    stage(lds1, lds0, sc1, sc0, kt + 1);
-  }
-  if (kt < nk) stage(lds0, lds1, sc0, sc1, kt);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA outlives the workgroup
 
-  // ---- epilogue: epi(acc) -> bf16, four consecutive n per store
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + 32 * j + r;
-    if (m >= M) continue;
-    uint16_t* crow = c + (size_t)m * N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (n0 + wn * 128 + 32 * i >= N) continue;        // N % 128 == 0: whole 32-column tiles
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
-        float y[4] = {acc[i][j][4 * qd], acc[i][j][4 * qd + 1], acc[i][j][4 * qd + 2], acc[i][j][4 * qd + 3]};
-        if (EPI >= 1) {
-          uint2 b = *(const uint2*)(bias + n);
-          y[0] += dev::bf16_lo(b.x);
-          y[1] += dev::bf16_hi(b.x);
-          y[2] += dev::bf16_lo(b.y);
-          y[3] += dev::bf16_hi(b.y);
-        }
-        if (EPI == 2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
-        }
-        uint2 o;
-        o.x = dev::pack_bf16x2(y[0], y[1]);
-        o.y = dev::pack_bf16x2(y[2], y[3]);
-        *(uint2*)(crow + n) = o;
-      }
-    }
+  // Tile ti's origin and its successor's.  The DMA runs two stages ahead, into the
+  // next tile near the end of this one.
+  int m0 = 0, n0 = 0, m0n = 0, n0n = 0;
+  origin(0, m0, n0);
+  if (my_tiles > 1) origin(1, m0n, n0n);
+
+  // Prologue: the first two stages in flight; wait; stage 0's scales and first-half fragments.
+  {
+    const bool nx1 = nk < 2;
+    dma_stage(lds0, sc0, m0, n0, 0, true);
+    dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_scales(sc0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f0w[i] = frag(lds0, wrow + 32 * i, x, 0, g);
+    f0a[i] = frag(lds0 + kOperand, arow + 32 * i, x, 0, g);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
+
+  // Global stage g uses buffer g & 1.  With an even number of stages per tile every
+  // tile starts in buffer 0; with an odd number the launcher gives each workgroup a
+  // single tile.  The K loop is unrolled by two so that every LDS pointer is a fixed
+  // object, and the DMA target of stage kt + 2 is chosen with scalar selects (no
+  // branch inside the loop body).
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const bool has_next = ti + 1 < my_tiles;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    auto one = [&](uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
+      const int kk = kt + 2;
+      const bool nx = kk >= nk;
+      stage(acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      one(lds0, lds1, sc0, sc1, kt);
+      one(lds1, lds0, sc1, sc0, kt + 1);
+    }
+    if (kt < nk) one(lds0, lds1, sc0, sc1, kt);
+    epilogue(acc, m0, n0);
+    m0 = m0n;
+    n0 = n0n;
+    if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA outlives the workgroup
 }
 
 template <int AK, int WK>
 hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int M, int N, int K,
                         const void* bias, int epi, void* c, hipStream_t stream) {
   const int tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
-  dim3 grid(tiles), block(kThreads);
+  // persistent (one workgroup per CU) when a tile has an even number of K stages;
+  // otherwise one workgroup per tile
+  const int cus = device_compute_units();
+  const int grid_n = ((K / kBK) % 2 != 0 || tiles < cus) ? tiles : cus;
+  dim3 grid(grid_n), block(kThreads);
   auto A = (const uint8_t*)a_q;
   auto As = (const uint8_t*)a_s;
   auto W = (const uint8_t*)w_q;
@@ -266,7 +310,7 @@ hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const
 }  // namespace
 
 // Shapes reaching here are validated: M, N, K positive multiples of 128, kinds 0/1, epi 0..2.
-// Partial 256-tiles (M or N = 128 mod 256) load clamped rows and skip their stores.
+// Partial 256-tiles (M or N = 128 mod 256) skip the stores of their missing half.
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q, const void* w_s,
                              int w_kind, int64_t M, int64_t N, int64_t K, const void* bias, int epi, void* c,
                              hipStream_t stream) {

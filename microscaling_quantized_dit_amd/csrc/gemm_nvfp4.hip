@@ -14,18 +14,24 @@
 // [2^-10, 2688], inside fp16's normal range, so val(q) * val(S) is exact in fp16
 // and the fp16 MFMA (v_mfma_f32_32x32x16_f16) multiplies exact dequantized values
 // with fp32 accumulation.  The global scales are applied once, in the epilogue.
-// One 16-K MFMA step is exactly one NVFP4 block, so every lane's 8 values of a
-// step share one scale.  Dequantization costs one VALU op per element
-// (fp4 -> fp16 pair conversion, then a packed fp16 multiply), hidden under MFMA.
+// Dequantization costs one VALU op per element per wave (fp4 -> fp16 pair
+// conversion, then a packed fp16 multiply) and runs under the MFMAs of the
+// previous K-step.
 //
 // fp16 operand layout (measured on gfx950): lane l holds row l % 32, K
 // [8g, 8g+8) of the 16-K step (g = l / 32); result D[8(v/4) + 4g + v%4][l % 32].
 // W is the first operand, A the second (each lane stores 4 consecutive n).
+// The K order inside an MFMA is free as long as both operands use the same one:
+// in a 64-K group lane group g reads the 32 consecutive values [32g, 32g+32) (one
+// 16-byte LDS read) and K-step j takes its values [8j, 8j+8).  Those 8 values sit
+// in NVFP4 block 2g + j/2 of the group, so each lane's step has a single scale.
 //
-// Tiling as the MXFP8 kernel: 256 x 256 per workgroup, 4 waves of 128 x 128,
-// 128 K (64 bytes) per LDS stage, two stages.  In LDS each row's 16 dwords are
-// regrouped so that one lane finds all 8 of its K-steps in 32 contiguous bytes
-// (two 16-byte reads), rows padded to 80 bytes against bank conflicts.
+// Tiling as the MXFP8 kernel: 256 x 256 output tiles, 4 waves of 128 x 128,
+// codes and scale dwords copied global -> LDS by buffer_load ... lds into two
+// stage buffers of 128 K (64-byte rows, XOR-swizzled), one 64-K group per half
+// stage with the mid-stage barrier between them; persistent over tiles.
+#include <type_traits>
+
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -34,22 +40,33 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;
-constexpr int kBK = 128;              // K elements per stage (64 bytes per row)
-constexpr int kRow = 64 + 16;         // padded LDS row (bytes)
-constexpr int kStage = 2 * kTile * kRow;
+constexpr int kBK = 128;                       // K values per stage
+constexpr int kRowB = kBK / 2;                 // 64 code bytes per row and stage
+constexpr int kOperand = kTile * kRowB;        // 16 KiB
+constexpr int kStage = 2 * kOperand;           // W then A
 constexpr int kGroupM = 4;
 
-// 8 packed E2M1 values (one dword, element 2j in the low nibble of byte j) times
-// the fp16 scale s -> v8h, exactly.
+// Swizzle of the four 16-byte chunks of a 64-byte LDS row: the 16 rows read by a
+// quarter-wave land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// This lane's 16 code bytes of 64-K group G in row R (logical chunk 2G + g).
+__device__ __forceinline__ uint4 codes(const uint8_t* tile, int R, int x, int G, int g) {
+  return *(const uint4*)(tile + R * kRowB + (((2 * G + g) ^ x) << 4));
+}
+
+// 8 packed E2M1 values (element 2e in the low nibble of byte e) times the fp16
+// scale s -> v8h, exactly.
 __device__ __forceinline__ v8h dequant8(uint32_t d, _Float16 s) {
   v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
   v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
   v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
   v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
-  v2h ss = {s, s};
+  const v2h ss = {s, s};
   p0 *= ss;
   p1 *= ss;
   p2 *= ss;
@@ -57,14 +74,14 @@ __device__ __forceinline__ v8h dequant8(uint32_t d, _Float16 s) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// The 8 E4M3 block scales of one row for this stage (a uint2) -> 8 fp16 values.
-__device__ __forceinline__ void scales8(uint2 b, _Float16 (&s)[8]) {
-  v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 1.0f, false);
-  v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.x, 1.0f, true);
-  v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, false);
-  v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b.y, 1.0f, true);
-  s[0] = a0[0]; s[1] = a0[1]; s[2] = a1[0]; s[3] = a1[1];
-  s[4] = a2[0]; s[5] = a2[1]; s[6] = a3[0]; s[7] = a3[1];
+// The two E4M3 block scales in the low 16 bits of w -> fp16 pair (exact).
+__device__ __forceinline__ v2h scale_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t word(const uint4& v) {
+  return J == 0 ? v.x : J == 1 ? v.y : J == 2 ? v.z : v.w;
 }
 
 template <int EPI>
@@ -72,161 +89,278 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const float* __restrict__ ag,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const float* __restrict__ wg,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  // two stage buffers (codes; scale dwords [W d0, W d1, A d0, A d1][row]) as distinct objects
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
+  __shared__ __attribute__((aligned(16))) uint32_t sc0[4 * kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t sc1[4 * kTile];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
-  const int wg_id = dev::xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = kGroupM * tiles_n;
-  const int first_m = (wg_id / per_group) * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (wg_id % per_group) % gsize;
-  const int tn = (wg_id % per_group) / gsize;
-  const int m0 = tm * kTile, n0 = tn * kTile;
+  const int n_tiles = tiles_m * tiles_n;
+  const int nk = K / kBK;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  auto origin = [&](int ti, int& m0, int& n0) {
+    const int v = blockIdx.x + ti * gridDim.x;
+    const int wg_id = dev::xcd_remap(v, n_tiles);
+    const int per_group = kGroupM * tiles_n;
+    const int first_m = (wg_id / per_group) * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    m0 = (first_m + (wg_id % per_group) % gsize) * kTile;
+    n0 = ((wg_id % per_group) / gsize) * kTile;
+  };
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int r = lane & 31, g = lane >> 5;
-  const int KP = K / 2, KS = K / 16;   // bytes per row: codes, scales
+  const int KP = K / 2, KS = K / 16;    // bytes per row: codes, scales
 
+  // 32-bit offsets: operands are < 2 GiB (checked by the host)
   const auto rw = __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, N * KP, 0x00020000);
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * KP, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KS, 0x00020000);
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc((void*)as_, (short)0, M * KS, 0x00020000);
-  // staging: thread t copies 16-byte chunk (t & 3) of rows (t >> 2) + 64 i, i = 0..3
-  const int cc = t & 3;
-  const int voff = (t >> 2) * KP + cc * 16;
-  // LDS regrouping: row dword o = 2*step + half goes to slot 8*half + step; chunk cc
-  // holds dwords 4cc..4cc+3 = (step 2cc, half 0/1), (step 2cc+1, half 0/1).
-  const int loff = (t >> 2) * kRow + 8 * cc;
-  const int vsw = (wn * 128 + r) * KS, vsa = (wm * 128 + r) * KS;
 
-  uint4 stw[4], sta[4];
-  uint2 nscw[4], nsca[4];
-  auto load_stage = [&](int k0) {   // k0 in elements
+  // Global -> LDS: one buffer_load ... lds moves 1 KiB per wave = 16 rows of 64 B
+  // (lane i -> row i / 4, physical chunk i % 4, i.e. global chunk (i % 4) ^ swz).
+  // Rows 16j + i/4 have swz = (i >> 4) & 3 whatever j, so one lane offset serves
+  // all four loads of a wave's 64 rows.  Scale dwords: lane i -> row 64w + i.
+  const int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  const int vsc = lane * KS;
+  // Every load stays inside its operand: a wave's 64 rows lie wholly inside or past
+  // M (N); rows past the end, and stages after the last tile, read rows [0, 64).
+  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
+    const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
+    const bool vw = valid && rw0 < N, va = valid && ra0 < M;
+    const int off_w = vw ? rw0 * KP + k0 / 2 : 0, off_a = va ? ra0 * KP + k0 / 2 : 0;
+    const int off_sw = vw ? rw0 * KS + k0 / 16 : 0, off_sa = va ? ra0 * KS + k0 / 16 : 0;
+    uint8_t* base = buf + wave * 64 * kRowB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      stw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff, (n0 + 64 * i) * KP + k0 / 2, 0));
-      sta[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff, (m0 + 64 * i) * KP + k0 / 2, 0));
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 16 * kRowB), 16, voff,
+                                               off_w + j * 16 * KP, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 16 * kRowB), 16, voff,
+                                               off_a + j * 16 * KP, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      nscw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsw, vsw, (n0 + 32 * i) * KS + k0 / 16, 0));
-      nsca[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsa, vsa, (m0 + 32 * i) * KS + k0 / 16, 0));
-    }
-  };
-  auto store_stage = [&](int st) {
-    uint8_t* base = lds + st * kStage + loff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint8_t* pw = base + 64 * i * kRow;
-      *(uint2*)(pw) = make_uint2(stw[i].x, stw[i].z);
-      *(uint2*)(pw + 32) = make_uint2(stw[i].y, stw[i].w);
-      uint8_t* pa = base + kTile * kRow + 64 * i * kRow;
-      *(uint2*)(pa) = make_uint2(sta[i].x, sta[i].z);
-      *(uint2*)(pa + 32) = make_uint2(sta[i].y, sta[i].w);
+    for (int d = 0; d < 2; ++d) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + d * kTile + wave * 64), 4, vsc, off_sw + 4 * d,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + (2 + d) * kTile + wave * 64), 4, vsc,
+                                               off_sa + 4 * d, 0, 0);
     }
   };
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
+  const int wrow = wn * 128 + r, arow = wm * 128 + r;
+  uint4 c0w[4], c0a[4], c1w[4], c1a[4];     // codes of the stage's 64-K groups 0 and 1
+  v2h s0w[4], s0a[4], s1w[4], s1a[4];       // their scales: {steps 0-1, steps 2-3}
+  v8h dw[2][4], da[2][4];                   // dequantized operands, double-buffered by K-step
+  uint32_t rs1w[4], rs1a[4];                // raw group-1 scale dwords of the next stage
 
-  const int nk = K / kBK;
-  load_stage(0);
-  store_stage(0);
-  uint2 scw[4], sca[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { scw[i] = nscw[i]; sca[i] = nsca[i]; }
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) load_stage((kt + 1) * kBK);
-    const uint8_t* wl = lds + st * kStage + (wn * 128 + r) * kRow + 32 * g;
-    const uint8_t* al = lds + st * kStage + kTile * kRow + (wm * 128 + r) * kRow + 32 * g;
-    uint4 wd[4][2], ad[4][2];
-    _Float16 sw[4][8], sa[4][8];
+  // Scale dwords of a stage: group 0's are converted at once (the previous group 0
+  // is finished by then), group 1's kept raw until the current group 1 is done.
+  // Lane group g uses blocks 2g, 2g + 1 of each group: the g-th 16-bit half.
+  auto read_scales = [&](const uint32_t* sc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wd[i][0] = *(const uint4*)(wl + 32 * i * kRow);
-      wd[i][1] = *(const uint4*)(wl + 32 * i * kRow + 16);
-      ad[i][0] = *(const uint4*)(al + 32 * i * kRow);
-      ad[i][1] = *(const uint4*)(al + 32 * i * kRow + 16);
-      scales8(scw[i], sw[i]);
-      scales8(sca[i], sa[i]);
+      s0w[i] = scale_pair(sc[wrow + 32 * i] >> (16 * g));
+      rs1w[i] = sc[kTile + wrow + 32 * i];
+      s0a[i] = scale_pair(sc[2 * kTile + arow + 32 * i] >> (16 * g));
+      rs1a[i] = sc[3 * kTile + arow + 32 * i];
     }
+  };
+  auto convert_scales = [&]() {
 #pragma unroll
-    for (int step = 0; step < 8; ++step) {
-      v8h wf[4], af[4];
+    for (int i = 0; i < 4; ++i) {
+      s1w[i] = scale_pair(rs1w[i] >> (16 * g));
+      s1a[i] = scale_pair(rs1a[i] >> (16 * g));
+    }
+  };
+  auto read_codes = [&](uint4 (&cw)[4], uint4 (&ca)[4], const uint8_t* buf, int G) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cw[i] = codes(buf, wrow + 32 * i, x, G, g);
+      ca[i] = codes(buf + kOperand, arow + 32 * i, x, G, g);
+    }
+  };
+  // dequantize K-step J of a group into buffer B
+  auto dequant = [&](auto B_, auto J_, const uint4 (&cw)[4], const uint4 (&ca)[4], const v2h (&sw)[4],
+                     const v2h (&sa)[4]) {
+    constexpr int B = decltype(B_)::value, J = decltype(J_)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dw[B][i] = dequant8(word<J>(cw[i]), sw[i][J >> 1]);
+      da[B][i] = dequant8(word<J>(ca[i]), sa[i][J >> 1]);
+    }
+  };
+  auto mfma_step = [&](v16f (&acc)[4][4], auto B_) {
+    constexpr int B = decltype(B_)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(dw[B][i], da[B][j], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // 16 MFMAs, each followed by 4 of the next step's dequantization ops (and, for the
+  // first `reads` MFMAs, one LDS read; for the first `vmem` ones, one DMA load)
+  auto interleave = [&](int reads, int vmem) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const float alpha = (*ag) * (*wg);
+  auto epilogue = [&](const v16f (&acc)[4][4], int m0, int n0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 128 + 32 * j + r;
+      uint16_t* crow = c + (size_t)m * N;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4& x = wd[i][step >> 2];
-        const uint4& y = ad[i][step >> 2];
-        const int e = step & 3;
-        wf[i] = dequant8(e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w, sw[i][step]);
-        af[i] = dequant8(e == 0 ? y.x : e == 1 ? y.y : e == 2 ? y.z : y.w, sa[i][step]);
+        // M, N are multiples of 128: whole 32-row / 32-column MFMA tiles are in or out
+        if (m0 + wm * 128 + 32 * j < M && n0 + wn * 128 + 32 * i < N) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
+            float y[4] = {alpha * acc[i][j][4 * qd], alpha * acc[i][j][4 * qd + 1], alpha * acc[i][j][4 * qd + 2],
+                          alpha * acc[i][j][4 * qd + 3]};
+            if (EPI >= 1) {
+              uint2 b = *(const uint2*)(bias + n);
+              y[0] += dev::bf16_lo(b.x);
+              y[1] += dev::bf16_hi(b.x);
+              y[2] += dev::bf16_lo(b.y);
+              y[3] += dev::bf16_hi(b.y);
+            }
+            if (EPI == 2) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
+            }
+            uint2 o;
+            o.x = dev::pack_bf16x2(y[0], y[1]);
+            o.y = dev::pack_bf16x2(y[2], y[3]);
+            *(uint2*)(crow + n) = o;
+          }
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      store_stage(st ^ 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { scw[i] = nscw[i]; sca[i] = nsca[i]; }
-    }
-    __syncthreads();
-  }
+  };
 
-  // ---- epilogue: epi(alpha * acc) -> bf16
-  const float alpha = (*ag) * (*wg);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + 32 * j + r;
-    if (m >= M) continue;
-    uint16_t* crow = c + (size_t)m * N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (n0 + wn * 128 + 32 * i >= N) continue;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
-        float y[4] = {alpha * acc[i][j][4 * qd], alpha * acc[i][j][4 * qd + 1], alpha * acc[i][j][4 * qd + 2],
-                      alpha * acc[i][j][4 * qd + 3]};
-        if (EPI >= 1) {
-          uint2 b = *(const uint2*)(bias + n);
-          y[0] += dev::bf16_lo(b.x);
-          y[1] += dev::bf16_hi(b.x);
-          y[2] += dev::bf16_lo(b.y);
-          y[3] += dev::bf16_hi(b.y);
-        }
-        if (EPI == 2) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
-        }
-        uint2 o;
-        o.x = dev::pack_bf16x2(y[0], y[1]);
-        o.y = dev::pack_bf16x2(y[2], y[3]);
-        *(uint2*)(crow + n) = o;
-      }
-    }
+  // One stage (cur holds it, nxt the next one):
+  //   A: group 0's four K-steps on MFMA || LDS reads of group 1's codes; the last
+  //      step dequantizes group 1's first step
+  //   B: wait for the next stage's DMA and this wave's reads, barrier
+  //   C: group 1's K-steps || LDS reads of the next stage's scales and group-0 codes,
+  //      DMA of the stage after next into cur; the last step dequantizes the next
+  //      stage's first step.
+  // On entry dw/da[0] hold group 0's first step, dequantized.
+  auto stage = [&](v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int dm0,
+                   int dn0, int dk0, bool dvalid) {
+    // ---- A
+    read_codes(c1w, c1a, cur, 1);
+    mfma_step(acc, I0());
+    dequant(I1(), I1(), c0w, c0a, s0w, s0a);
+    interleave(8, 0);
+    mfma_step(acc, I1());
+    dequant(I0(), I2(), c0w, c0a, s0w, s0a);
+    interleave(0, 0);
+    mfma_step(acc, I0());
+    dequant(I1(), I3(), c0w, c0a, s0w, s0a);
+    interleave(0, 0);
+    mfma_step(acc, I1());
+    dequant(I0(), I0(), c1w, c1a, s1w, s1a);
+    interleave(0, 0);
+    // ---- B
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    // ---- C
+    read_scales(snxt);
+    read_codes(c0w, c0a, nxt, 0);
+    dma_stage(cur, scur, dm0, dn0, dk0, dvalid);
+    mfma_step(acc, I0());
+    dequant(I1(), I1(), c1w, c1a, s1w, s1a);
+    interleave(16, 12);
+    mfma_step(acc, I1());
+    dequant(I0(), I2(), c1w, c1a, s1w, s1a);
+    interleave(8, 0);
+    mfma_step(acc, I0());
+    dequant(I1(), I3(), c1w, c1a, s1w, s1a);
+    interleave(0, 0);
+    mfma_step(acc, I1());
+    convert_scales();
+    dequant(I0(), I0(), c0w, c0a, s0w, s0a);
+    interleave(0, 0);
+  };
+
+  int m0 = 0, n0 = 0, m0n = 0, n0n = 0;
+  origin(0, m0, n0);
+  if (my_tiles > 1) origin(1, m0n, n0n);
+
+  // Prologue: the first two stages in flight; wait; stage 0's scales, codes and first step.
+  {
+    const bool nx1 = nk < 2;
+    dma_stage(lds0, sc0, m0, n0, 0, true);
+    dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_scales(sc0);
+  read_codes(c0w, c0a, lds0, 0);
+  convert_scales();
+  dequant(I0(), I0(), c0w, c0a, s0w, s0a);
+
+  // Global stage s uses buffer s & 1; with an even number of stages per tile every
+  // tile starts in buffer 0 (the launcher gives each workgroup one tile otherwise).
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const bool has_next = ti + 1 < my_tiles;
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    auto one = [&](uint8_t* b0, uint8_t* b1, uint32_t* t0, uint32_t* t1, int kt) {
+      const int kk = kt + 2;
+      const bool nx = kk >= nk;
+      stage(acc, b0, b1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next);
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      one(lds0, lds1, sc0, sc1, kt);
+      one(lds1, lds0, sc1, sc0, kt + 1);
+    }
+    if (kt < nk) one(lds0, lds1, sc0, sc1, kt);
+    epilogue(acc, m0, n0);
+    m0 = m0n;
+    n0 = n0n;
+    if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA outlives the workgroup
 }
 
 }  // namespace
 
+// Shapes reaching here are validated: M, N, K positive multiples of 128, epi 0..2.
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q, const void* w_s,
                              const float* w_g, int64_t M, int64_t N, int64_t K, const void* bias, int epi, void* c,
                              hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
-  dim3 grid(tiles), block(kThreads);
+  // persistent (one workgroup per CU) when a tile has an even number of K stages;
+  // otherwise one workgroup per tile
+  const int cus = device_compute_units();
+  const int grid_n = ((k / kBK) % 2 != 0 || tiles < cus) ? tiles : cus;
+  dim3 grid(grid_n), block(kThreads);
   auto A = (const uint8_t*)a_q;
   auto As = (const uint8_t*)a_s;
   auto W = (const uint8_t*)w_q;

@@ -57,7 +57,22 @@ mxq_status launched(hipError_t e, const char* what) {
 
 constexpr int64_t kMax32 = (int64_t)1 << 31;
 
+std::atomic<int> g_cus[64];
+
 }  // namespace
+
+namespace mxq {
+int device_compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace mxq
 
 extern "C" {
 

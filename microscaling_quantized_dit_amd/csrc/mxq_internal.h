@@ -6,6 +6,9 @@
 
 namespace mxq {
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+int device_compute_units();
+
 // Host-side launchers (each returns the hipError_t of its launch).
 hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void* q, void* scales,
                                  hipStream_t stream);

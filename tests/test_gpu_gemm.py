@@ -158,6 +158,20 @@ def test_partial_tiles_and_k(mxq, M, N, K):
     _assert_close(*run_nv(mxq, NV(a), NV(w)), "nv %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("K", [256, 384, 512])
+def test_more_tiles_than_compute_units(mxq, K):
+    """310 output tiles of 256 x 256 (the last row and column of tiles half empty):
+    with an even number of 128-wide K stages a workgroup walks several tiles and
+    prefetches across tile boundaries; with an odd number each takes one.  Full
+    comparison, MXFP8 with bias + GELU and NVFP4."""
+    M, N = 2432, 7808
+    a = inputs.flux_activation(M, K, seed=K, stream="many/A")
+    w = inputs.weight(N, K, seed=K, stream="many/W")
+    b = inputs.bias(N, K, seed=K, stream="many/b")
+    _assert_close(*run_mx(mxq, MX(a, oracle.E4M3), MX(w, oracle.E4M3), bias=b, epi="bias_gelu"), "mx K=%d" % K)
+    _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias"), "nv K=%d" % K)
+
+
 def test_deterministic(mxq):
     import torch
     A = NV(inputs.flux_activation(512, 1024, seed=2, stream="det/A"))
