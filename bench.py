@@ -24,6 +24,7 @@ oracle is timed on a bounded sample of the same work (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,30 @@ NV_LINEARS = [  # name, N, K, epilogue   (M = 18432)
     ("linear2", 3072, 15360, "none"),
 ]
 M_MX, M_NV = 4608, 18432
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE per dispatch, scaled by a
+    1 GiB copy), or None when there is no record or the kernel's sources have
+    changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        try:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    if h.hexdigest() != rec["sha256"]:
+        return None
+    return rec
 
 
 def parse():
@@ -273,6 +298,11 @@ def main():
         achieved = per_launch / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    rec = measured_traffic(dom)
+    if rec is not None:
+        roofline["traffic"] = rec["bytes_per_launch"]
+        roofline["traffic_read"] = rec["read_bytes_per_launch"]
+        roofline["traffic_write"] = rec["write_bytes_per_launch"]
     roofline.update({"kernel": dom, "launches_per_step": d["launches"], "ops": d["ops"],
                      "avg_launch_ms": round(avg_ms, 4), "work_per_launch": per_launch,
                      "work_unit": d["unit"]})

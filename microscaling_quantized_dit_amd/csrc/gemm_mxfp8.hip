@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- B
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     // ---- C
     read_scales(snxt);
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     dma_stage(lds0, sc0, m0, n0, 0, true);
     dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
   read_scales(sc0);
 #pragma unroll
@@ -259,6 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // object, and the DMA target of stage kt + 2 is chosen with scalar selects (no
   // branch inside the loop body).
   for (int ti = 0; ti < my_tiles; ++ti) {
+    // Once per tile: lets the compiler's wait-count tracking retire register spill
+    // stores made outside the K loop, which it would otherwise wait for inside it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     const bool has_next = ti + 1 < my_tiles;
     v16f acc[4][4];
 #pragma unroll
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     n0 = n0n;
     if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outlives the workgroup
 }
 
 template <int AK, int WK>
