@@ -61,11 +61,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// GELU, tanh form: 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))).
+// GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
+// Since 1 + tanh(u) = 2 / (1 + e^(-2u)), this is y / (1 + 2^(-2u log2 e)): one
+// hardware exp2 and one reciprocal, each within about 1 ulp, with no cancellation
+// for large negative y (the quotient tends to -0) or overflow for large positive
+// y (the exponential tends to 0).
 __device__ __forceinline__ float gelu_tanh(float y) {
-  const float k0 = 0.7978845608028654f;
+  const float k0 = 0.7978845608028654f;             // sqrt(2/pi)
   const float k1 = 0.044715f;
-  return 0.5f * y * (1.0f + tanhf(k0 * (y + k1 * y * y * y)));
+  const float m2log2e = -2.0f * 1.4426950408889634f; // -2 log2(e)
+  const float u = k0 * (y + k1 * y * y * y);
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
 }
 
 // Remap a linear workgroup id so that ids placed round-robin on the 8 XCDs

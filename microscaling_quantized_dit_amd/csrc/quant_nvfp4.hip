@@ -21,7 +21,9 @@
 // Otherwise (an exact tie or a near tie, or a reciprocal outside the fp32
 // normal range) the decision is redone with exact fp64 comparisons: every
 // threshold (midpoint x S_b x s_g, or midpoint x 6 x s_g) has at most
-// 5 + 4 + 24 significant bits and is exact in fp64.
+// 5 + 4 + 24 significant bits and is exact in fp64.  The fallback is inlined
+// behind a branch that is almost never taken: as a called function it would give
+// every wave a private stack, which alone cost 40% of the kernel's speed.
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -75,7 +77,7 @@ __device__ __forceinline__ double e4m3_value(int c) {
 
 // Exact S_b code: the E4M3 code nearest to amax / (6 s_g), ties to the even code,
 // saturating at 448 (code 126).  Binary search on exact fp64 comparisons.
-__device__ __noinline__ int exact_block_scale(double amax, double six_sg) {
+__device__ __forceinline__ int exact_block_scale(double amax, double six_sg) {
   if (amax >= 448.0 * six_sg) return 126;
   int lo = 0, hi = 126;                  // invariant: val(lo) * d <= amax < val(hi) * d
   while (hi - lo > 1) {
@@ -91,7 +93,7 @@ __device__ __noinline__ int exact_block_scale(double amax, double six_sg) {
 // Exact E2M1 magnitude code of |x| / D (D = S_b s_g exact in fp64): count the
 // rounding midpoints passed; at a tie the even code wins, so the midpoints
 // between (0, 0.5), (1, 1.5), (2, 3), (4, 6) need a strict '>' and the others '>='.
-__device__ __noinline__ uint32_t exact_e2m1(double ax, double D) {
+__device__ __forceinline__ uint32_t exact_e2m1(double ax, double D) {
   uint32_t c = 0;
   c += ax > 0.25 * D;
   c += ax >= 0.75 * D;
@@ -101,6 +103,56 @@ __device__ __noinline__ uint32_t exact_e2m1(double ax, double D) {
   c += ax >= 3.5 * D;
   c += ax > 5.0 * D;
   return c;
+}
+
+// Exact codes of the eight values of a chunk for divisor S s_g (S > 0).
+__device__ __forceinline__ uint32_t exact_chunk(uint4 v, float S, float sg) {
+  const double Dd = (double)S * (double)sg;                 // exact (4 x 24 bits)
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t codes = 0;
+  for (int e = 0; e < 8; ++e) {
+    uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    double ax = (double)__uint_as_float((bits & 0x7FFFu) << 16);
+    uint32_t nib = exact_e2m1(ax, Dd) | ((bits >> 12) & 0x8u);
+    codes |= nib << (4 * e);
+  }
+  return codes;
+}
+
+// Is a > mid * k * sg, exactly?  (mk = mid * k exact in fp32, a within a factor
+// of two of mk * sg.)  mk * sg = p + e exactly (two-product by FMA, no underflow
+// for the magnitudes that reach here); a - p is exact (Sterbenz); so the sign of
+// a - mk * sg is that of (a - p) - e, decided by comparing a - p with e.  At an
+// exact tie the code with an even last bit wins.
+__device__ __forceinline__ bool round_up_at(float a, float mk, float sg, bool upper_even) {
+  const float p = mk * sg;
+  const float e = __builtin_fmaf(mk, sg, -p);
+  const float d = a - p;
+  return d > e || (d == e && upper_even);
+}
+
+// E2M1 magnitude code 0..7 -> value {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ float e2m1_mag(uint32_t c) {
+  return c < 2 ? 0.5f * (float)c : __builtin_ldexpf(1.0f + 0.5f * (float)(c & 1), (int)(c >> 1) - 1);
+}
+
+// Near-tie resolution for a chunk whose two bracketing encodings lo, hi differ:
+// where a value's two codes differ, exactly one rounding midpoint (between the
+// adjacent magnitudes) lies between the brackets; compare against it exactly.
+__device__ __forceinline__ uint32_t resolve_chunk(uint4 v, uint32_t lo, uint32_t hi, float S, float sg) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t nl = (lo >> (4 * e)) & 7u, nh = (hi >> (4 * e)) & 7u;
+    if (nl != nh) {
+      const float ax = __uint_as_float(((w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu) << 16);
+      const float mk = (e2m1_mag(nl) + e2m1_mag(nh)) * (0.5f * S);   // <= 7 significant bits
+      const uint32_t c = round_up_at(ax, mk, sg, (nh & 1u) == 0) ? nh : nl;
+      out = (out & ~(7u << (4 * e))) | (c << (4 * e));
+    }
+  }
+  return out;
 }
 
 // Eight bf16 values (one uint4) -> eight E2M1 codes (a dword, element 2j in the low
@@ -118,10 +170,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
                                                           const float* __restrict__ global_in,
                                                           const uint32_t* __restrict__ partials, int n_partials,
                                                           uint32_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                          float* __restrict__ global_out) {
+                                                          float* __restrict__ global_out, int reverse) {
   __shared__ uint32_t red[kThreads / 64];
   const int t = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll);
+  // with `reverse` workgroups take the slabs last to first: right after the amax
+  // pass, the tail of x that is still in the last-level cache is read first
+  const int64_t slab = reverse ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+  const int64_t base = slab * (kThreads * kUnroll);
   uint4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -142,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
     // IEEE (correctly rounded) fp32 division: RN_fp32(amax / 2688).
     sg = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 2688.0f;
   }
-  if (blockIdx.x == 0 && t == 0) *global_out = sg;
+  if (slab == 0 && t == 0) *global_out = sg;
 
   // ---- per-kernel constants: bracketing reciprocals of 6 s_g
   const double six_sg = 6.0 * (double)sg;                   // exact (3 x 24 bits)
@@ -159,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
     m = max(m, (uint32_t)__shfl_xor((int)m, 1));
     const float amax_b = __uint_as_float(m << 16);
 
-    // ---- S_b = RN_E4M3(amax_b / (6 s_g))
+    // ---- S_b = RN_E4M3(amax_b / (6 s_g)), from the two bracketing quotients
     int sb;
     {
       float ql = __builtin_amdgcn_fmed3f(amax_b * r6_lo, 0.0f, 448.0f);
@@ -167,40 +222,27 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
       int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ql, qh, 0, false);
       int cl = pk & 0xFF, ch = (pk >> 8) & 0xFF;
       sb = cl;
-      if (cl != ch || !fast6) sb = exact_block_scale((double)amax_b, six_sg);
+      if (__builtin_expect(!fast6, 0)) {
+        sb = exact_block_scale((double)amax_b, six_sg);
+      } else if (__builtin_expect(cl != ch, 0)) {
+        // one midpoint between the adjacent codes cl < ch: compare exactly
+        const float mk = (__builtin_amdgcn_cvt_f32_fp8(cl, 0) + __builtin_amdgcn_cvt_f32_fp8(ch, 0)) * 3.0f;
+        sb = round_up_at(amax_b, mk, sg, (ch & 1) == 0) ? ch : cl;
+      }
     }
-    const float S = (float)e4m3_value(sb);
+    const float S = __builtin_amdgcn_cvt_f32_fp8(sb, 0);      // E4M3 -> fp32, exact
 
-    // ---- codes: x / (S s_g), bracketed
-    uint32_t codes;
+    // ---- codes: x / (S s_g), bracketed.  S = 0 gives r = 0 and signed zeros.
     const float D = S * sg;
-    if (S == 0.0f) {
-      codes = encode8(v[u], 0.0f);                           // signed zeros
-    } else {
-      // exact path when the reciprocal would lose range, or when the block scale
-      // saturated (only a static scale can then push quotients far past 6)
-      bool exact = !(D >= 0x1p-126f) || sb == 126;
-      uint32_t lo = 0, hi = 0;
-      if (!exact) {
-        const float r = __builtin_amdgcn_rcpf(D);             // <= 1 ulp
-        lo = encode8(v[u], r * (1.0f - 0x1p-19f));
-        hi = encode8(v[u], r * (1.0f + 0x1p-19f));
-        exact = lo != hi;
-      }
-      codes = lo;
-      if (exact) {
-        const double Dd = (double)S * (double)sg;           // exact (4 x 24 bits)
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        codes = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t bits = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-          double ax = (double)__uint_as_float((bits & 0x7FFFu) << 16);
-          uint32_t nib = exact_e2m1(ax, Dd) | ((bits >> 12) & 0x8u);
-          codes |= nib << (4 * i);
-        }
-      }
-    }
+    const float r = S == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(D);   // <= 1 ulp
+    uint32_t codes = encode8(v[u], r * (1.0f - 0x1p-19f));
+    const uint32_t hi = encode8(v[u], r * (1.0f + 0x1p-19f));
+    // fp64 path for a tiny divisor (reciprocal or two-product out of range) or a
+    // saturated block scale (only a static s_g can then push quotients far past
+    // 6); otherwise a midpoint between the brackets is settled exactly in fp32
+    const bool slow = S != 0.0f && (!(D >= 0x1p-100f) || sb == 126);
+    if (__builtin_expect(slow, 0)) codes = exact_chunk(v[u], S, sg);
+    else if (__builtin_expect(S != 0.0f && codes != hi, 0)) codes = resolve_chunk(v[u], codes, hi, S, sg);
     if (c < n_chunks) {
       q[c] = codes;
       if ((t & 1) == 0) s[c >> 1] = (uint8_t)sb;
@@ -234,7 +276,8 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
   const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x,
-                     n_chunks, global_in, partials, n_partials, (uint32_t*)q, (uint8_t*)scales, global_out);
+                     n_chunks, global_in, partials, n_partials, (uint32_t*)q, (uint8_t*)scales, global_out,
+                     global_in ? 0 : 1);
   return hipGetLastError();
 }
 
