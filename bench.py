@@ -161,6 +161,50 @@ class Workload:
         return w
 
 
+def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
+    """The single-stream NVFP4 activation quantizers with a static, calibrated
+    decode scale instead of the dynamic one: calibration folds two synthetic
+    activations per linear (the step's recipe, other seeds, 4608 rows) into the
+    scale on the GPU; then the static (one-pass) and dynamic (two-pass)
+    quantizers are timed back to back on the step's activation."""
+    out = {"calibration": "2 synthetic activations per linear (4608 rows each, same recipe, other seeds)"}
+    stream = torch.cuda.current_stream()
+    for L in wl.nv:
+        running = None
+        for i in range(2):
+            cal = inputs.to_torch(inputs.flux_activation(4608, L["K"], seed=0, stream="bench/%s/calib%d" % (L["name"], i)),
+                                  "cuda")
+            running = mxq.nvfp4_calibrate(cal, running)
+            del cal
+        g = torch.empty((1,), dtype=torch.float32, device="cuda")
+
+        def run_static():
+            mxq.quantize_nvfp4(L["x"], global_scale=running, out=(L["aq"], L["as_"], g))
+
+        def run_dynamic():
+            mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], g), workspace=L["wsb"])
+
+        res = {}
+        for tag, f in (("static", run_static), ("dynamic", run_dynamic)):
+            for _ in range(3):
+                f()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                f()
+            b.record(stream)
+            torch.cuda.synchronize()
+            res[tag] = a.elapsed_time(b) / reps
+        n = M_NV * L["K"]
+        nbytes = 2 * n + n // 2 + n // 16 + 4
+        rate = nbytes / (res["static"] * 1e-3) / 1e9
+        out["quant_nvfp4_" + L["name"]] = {
+            "static_ms": round(res["static"], 4), "dynamic_ms": round(res["dynamic"], 4),
+            "static_GB/s": round(rate, 1), "static_frac_of_hbm": round(rate / PEAK_HBM_GBPS, 4),
+            "calibrated_scale": float(running[0])}
+    return out
+
+
 def cpu_baseline(rows_per_linear: int):
     """The oracle (as it is) on a bounded sample: `rows_per_linear` activation rows of
     every linear of the step, quantized (dynamic scales over the sampled rows) and
@@ -335,6 +379,7 @@ def main():
         "ops": per_op,
         "roofline": roofline,
     }
+    result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)

@@ -125,6 +125,27 @@ mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols,
                               void* stream);
 
 /*
+ * Static-scale calibration for NVFP4 activations [P5 step 1 "校准": run a small
+ * batch through the model and record each layer's maximum, from which the scale
+ * that avoids truncation is set; P1 step 2 names the per-tensor scale].
+ *   x             : bf16 [rows, cols], device: one calibration tensor.
+ *   rows, cols    : > 0, cols a multiple of 16.
+ *   running_scale : device fp32, read and written:
+ *                   running_scale = max(running_scale, RN_fp32(amax(x) / 2688)),
+ *                   where an all-zero x contributes 0.  Set it to 0 before the
+ *                   first calibration tensor.  After the last one it is
+ *                   RN_fp32(max amax / 2688), the decode scale the dynamic mode
+ *                   would choose for the largest calibration tensor, and can be
+ *                   passed as global_scale_in of mxq_quantize_nvfp4 (one pass per
+ *                   call instead of two) as long as it is positive.  Values
+ *                   beyond the calibrated range then saturate to +-6 x S_b.
+ *   workspace     : as for mxq_quantize_nvfp4 (same size query).
+ * Calls that share running_scale or the workspace must be ordered on one stream.
+ */
+mxq_status mxq_nvfp4_calibrate(const void* x, int64_t rows, int64_t cols, float* running_scale,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * MXFP8 block-scaled GEMM [P3: every nn.Linear runs quantized; P2 §5.2: 128 alignment].
  *   C[m, n] = epi( sum_k val(a_q[m,k]) 2^(a_s[m,k/32]-127) val(w_q[n,k]) 2^(w_s[n,k/32]-127)
  *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.

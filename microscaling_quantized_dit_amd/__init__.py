@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "load", "MXQError", "E4M3", "E5M2", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
-    "quantize_mxfp8", "quantize_nvfp4", "nvfp4_workspace_size", "gemm_mxfp8", "gemm_nvfp4",
+    "quantize_mxfp8", "quantize_nvfp4", "nvfp4_workspace_size", "nvfp4_calibrate", "gemm_mxfp8", "gemm_nvfp4",
     "library_path",
 ]
 
@@ -33,7 +33,7 @@ _lock = threading.Lock()
 _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
-           "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_status_string", "mxq_last_error"]
+           "mxq_nvfp4_calibrate", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_status_string", "mxq_last_error"]
 
 
 class MXQError(RuntimeError):
@@ -63,13 +63,15 @@ def load():
         lib.mxq_quantize_nvfp4_workspace_size.argtypes = [i64, i64]
         lib.mxq_quantize_nvfp4_workspace_size.restype = sz
         lib.mxq_quantize_nvfp4.argtypes = [P, i64, i64, P, P, P, P, P, sz, P]
+        lib.mxq_nvfp4_calibrate.argtypes = [P, i64, i64, P, P, sz, P]
         lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P]
         lib.mxq_status_string.argtypes = [i32]
         lib.mxq_status_string.restype = ctypes.c_char_p
         lib.mxq_last_error.argtypes = []
         lib.mxq_last_error.restype = ctypes.c_char_p
-        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4"):
+        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_nvfp4_calibrate", "mxq_gemm_mxfp8",
+                  "mxq_gemm_nvfp4"):
             getattr(lib, f).restype = i32
         _lib = lib
         return lib
@@ -159,6 +161,28 @@ def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None):
     _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _ptr(g),
                                   _ptr(workspace), ws_bytes, _stream(stream)))
     return q, s, g
+
+
+def nvfp4_calibrate(x, running=None, workspace=None, stream=None):
+    """Fold one calibration tensor into a static NVFP4 decode scale:
+    running = max(running, RN_fp32(amax(x) / 2688)).  running: a 1-element fp32
+    CUDA tensor (zero-initialised here when None); returned for chaining and for
+    quantize_nvfp4(x, global_scale=running)."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if running is None:
+        running = torch.zeros((1,), dtype=torch.float32, device=x.device)
+    _need(running, torch.float32, "running", x.device)
+    ws_bytes = nvfp4_workspace_size(R, C)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.mxq_nvfp4_calibrate(_ptr(x), R, C, _ptr(running), _ptr(workspace), ws_bytes, _stream(stream)))
+    return running
 
 
 # ------------------------------------------------------------------------ GEMMs

@@ -121,6 +121,26 @@ mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, const f
                   "mxq_quantize_nvfp4 launch");
 }
 
+mxq_status mxq_nvfp4_calibrate(const void* x, int64_t rows, int64_t cols, float* running_scale, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (!x || !running_scale) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  if (rows <= 0 || cols <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "rows and cols must be positive");
+  if (cols % 16 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (rows > INT64_MAX / cols) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "rows * cols overflows");
+  if (!aligned16(x)) return fail(MXQ_ERROR_MISALIGNED, "x must be 16-byte aligned");
+  if ((uintptr_t)running_scale & 3u) return fail(MXQ_ERROR_MISALIGNED, "running_scale must be 4-byte aligned");
+  const size_t need = mxq_quantize_nvfp4_workspace_size(rows, cols);
+  if (!workspace || ws_bytes < need)
+    return fail(MXQ_ERROR_WORKSPACE, "calibration needs a %zu-byte workspace (got %zu)", need,
+                workspace ? ws_bytes : (size_t)0);
+  if ((uintptr_t)workspace & 3u) return fail(MXQ_ERROR_MISALIGNED, "workspace must be 4-byte aligned");
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_nvfp4_calibrate(x, rows * cols, running_scale, (uint32_t*)workspace,
+                                              (hipStream_t)stream),
+                  "mxq_nvfp4_calibrate launch");
+}
+
 static mxq_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c,
                                     int64_t a_row_bytes_num, int64_t a_row_bytes_den) {
   if (!c) return fail(MXQ_ERROR_INVALID_VALUE, "null output pointer");

@@ -19,6 +19,10 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
                                  void* scales, float* global_out, uint32_t* partials,
                                  hipStream_t stream);
 
+// running = max(running, RN_fp32(amax(x) / 2688)); partials as for the quantizer.
+hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running, uint32_t* partials,
+                                  hipStream_t stream);
+
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q,
                              const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
                              const void* bias, int epi, void* c, hipStream_t stream);

@@ -250,7 +250,37 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   }
 }
 
+// Calibration fold: running = max(running, RN_fp32(amax / 2688)) over the partial
+// maxima of one calibration tensor (an all-zero tensor contributes 0).  One
+// workgroup; the caller orders calls on one stream.
+__global__ __launch_bounds__(kThreads) void k_calib_fold(const uint32_t* __restrict__ partials, int n_partials,
+                                                         float* __restrict__ running) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int t = threadIdx.x;
+  uint32_t m = t < n_partials ? partials[t] : 0u;
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float sg = amax == 0 ? 0.0f : __uint_as_float(amax << 16) / 2688.0f;   // IEEE division
+    *running = fmaxf(*running, sg);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running, uint32_t* partials,
+                                  hipStream_t stream) {
+  const int64_t n_chunks = n_elems / 8;
+  const int n_partials = nvfp4_amax_partials(n_elems);
+  hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x, n_chunks,
+                     partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_calib_fold, dim3(1), dim3(kThreads), 0, stream, partials, n_partials, running);
+  return hipGetLastError();
+}
 
 int nvfp4_amax_partials(int64_t n_elems) {
   const int64_t n_chunks = n_elems / 8;

@@ -56,6 +56,7 @@ def _load():
             "orc_rn_fp32_div": (f32, [f64, f64]),
             "orc_quantize_mxfp8": (i32, [P, i64, i64, i32, P, P]),
             "orc_nvfp4_global_scale": (f32, [P, i64]),
+            "orc_nvfp4_calibrate": (f32, [P, i64, f32]),
             "orc_quantize_nvfp4": (i32, [P, i64, i64, P, P, P, P]),
             "orc_dequant_mxfp8": (None, [P, P, i64, i32, P, i64, P]),
             "orc_dequant_nvfp4": (None, [P, P, f32, i64, P, i64, P]),
@@ -136,6 +137,16 @@ def quantize_mxfp8(x, fmt: int = E4M3):
 def nvfp4_global_scale(x) -> np.float32:
     a = _as_u16(x)
     return np.float32(_load().orc_nvfp4_global_scale(_ptr(a), a.size))
+
+
+def nvfp4_calibrate(batches, running: float = 0.0) -> np.float32:
+    """Static NVFP4 decode scale from calibration tensors: the running maximum of
+    RN_fp32(amax / 2688) over the batches, starting from `running`."""
+    r = np.float32(running)
+    for x in batches:
+        a = _as_u16(x)
+        r = np.float32(_load().orc_nvfp4_calibrate(_ptr(a), a.size, float(r)))
+    return r
 
 
 def quantize_nvfp4(x, global_scale=None):

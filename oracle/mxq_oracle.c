@@ -232,6 +232,17 @@ float orc_nvfp4_global_scale(const uint16_t* x, int64_t n) {
     return orc_rn_fp32_div(amax, 6.0 * 448.0);
 }
 
+/* Static-scale calibration (page "FP8量化技术提升SD3.5在低带宽环境下的响应速度",
+ * step 1: record each layer's maximum over a calibration batch and set the scale
+ * so that nothing is truncated).  Folds one calibration tensor into the running
+ * decode scale: max(running, RN_fp32(amax / 2688)); an all-zero tensor adds 0. */
+float orc_nvfp4_calibrate(const uint16_t* x, int64_t n, float running) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) amax = fmax(amax, fabs(orc_bf16_value(x[i])));
+    const float s = amax == 0.0 ? 0.0f : orc_rn_fp32_div(amax, 6.0 * 448.0);
+    return s > running ? s : running;
+}
+
 /* Quantize bf16 x[rows, cols] (blocks of 16 along cols) into packed E2M1 codes
  * q[rows, cols/2] (element 2j low nibble), E4M3 block scales[rows, cols/16] and
  * the fp32 global decode scale.  global_in: NULL for the dynamic scale, else

@@ -90,6 +90,22 @@ def test_quantize_nvfp4_validation(lib):
     assert call(wsb=need - 4) == WORKSPACE
 
 
+def test_nvfp4_calibrate_validation(lib):
+    need = lib.mxq_quantize_nvfp4_workspace_size(4, 64)
+
+    def call(x=FAKE, rows=4, cols=64, run=FAKE, w=FAKE2, wsb=need):
+        return lib.mxq_nvfp4_calibrate(x, rows, cols, run, w, wsb, None)
+
+    assert call(x=None) == INVALID
+    assert call(run=None) == INVALID
+    assert call(rows=-1) == INVALID
+    assert call(cols=40) == SHAPE
+    assert call(x=MIS) == MISALIGNED
+    assert call(run=FAKE + 2) == MISALIGNED
+    assert call(w=None) == WORKSPACE
+    assert call(wsb=need - 4) == WORKSPACE
+
+
 def _g8(lib, M=128, N=256, K=256, bias=None, epi=0, c=FAKE, a=FAKE, ak=0, wk=0):
     return lib.mxq_gemm_mxfp8(a, FAKE2, ak, FAKE, FAKE2, wk, M, N, K, bias, epi, c, None)
 

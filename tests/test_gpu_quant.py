@@ -167,3 +167,24 @@ def test_deterministic(mxq):
     b = mxq.quantize_mxfp8(x)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+# ------------------------------------- static-scale calibration (P5 step 1)
+
+def test_nvfp4_static_calibration(mxq):
+    """Calibrated static decode scale: folded on the GPU over three calibration
+    activations (and an all-zero one), bit-equal to the oracle's; then a fresh
+    activation, partly beyond the calibrated range, quantized statically with it."""
+    import torch
+    batches = [inputs.flux_activation(64, 3072, seed=s, stream="calib/%d" % s) for s in range(3)]
+    running = None
+    for b in batches + [np.zeros((16, 3072), np.uint16)]:
+        running = mxq.nvfp4_calibrate(_dev(b), running)
+    g = np.float32(_np(running)[0])
+    assert g.tobytes() == oracle.nvfp4_calibrate(batches).tobytes()
+    fresh = inputs.flux_activation(128, 3072, seed=9, stream="calib/fresh")
+    hot = inputs.gaussian(8, 3072, 400.0, seed=9, stream="calib/hot")
+    _check_nv(mxq, np.concatenate([fresh, hot]), static=float(g))
+    # a running scale that already exceeds the tensor's stays put
+    r = torch.tensor([1e3], dtype=torch.float32, device="cuda")
+    assert float(mxq.nvfp4_calibrate(_dev(batches[0]), r)[0]) == 1e3

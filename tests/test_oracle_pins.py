@@ -364,3 +364,43 @@ def test_gelu_tanh_epilogue():
     ref = torch.nn.functional.gelu(torch.from_numpy(pre), approximate="tanh").numpy()
     assert np.allclose(y, ref, rtol=1e-14, atol=1e-300)
     assert np.allclose(y[0] - y[1], pre[0], rtol=1e-13)
+
+
+# ------------------------------ static-scale calibration (NEXT-3 row, P5 step 1)
+
+def _unpack_nibbles(q):
+    q = np.asarray(q)
+    out = np.empty((q.shape[0], q.shape[1] * 2), np.uint8)
+    out[:, 0::2] = q & 0xF
+    out[:, 1::2] = q >> 4
+    return out
+
+
+def test_calibrated_scale_pins():
+    """The calibrated decode scale is RN_fp32(max amax / 2688) over the
+    calibration tensors (exact rational arithmetic), whatever their order; an
+    all-zero tensor adds nothing; the tensor with the largest amax quantized
+    statically with it reproduces its own dynamic quantization; and a tensor
+    beyond the calibrated range quantizes (with saturation) exactly as the
+    rational definition says."""
+    batches = [inputs.gaussian(4, 64, std, seed=7, stream="calib/%d" % i) for i, std in enumerate((0.5, 3.0, 0.01))]
+    zero = np.zeros((2, 32), np.uint16)
+    g = oracle.nvfp4_calibrate(batches + [zero])
+    amax = max(abs(fr.bf16_value(int(v))) for b in batches for v in b.reshape(-1))
+    assert Fr(float(g)) == fr.rn_fp32(amax / 2688)
+    assert oracle.nvfp4_calibrate(list(reversed(batches))).tobytes() == g.tobytes()
+    assert oracle.nvfp4_calibrate([zero]) == 0.0
+    assert oracle.nvfp4_calibrate([zero], running=0.5) == np.float32(0.5)
+    big = batches[1]
+    q_dyn, s_dyn, g_dyn = oracle.quantize_nvfp4(big)
+    q_st, s_st, g_st = oracle.quantize_nvfp4(big, global_scale=g)
+    assert g_dyn.tobytes() == g.tobytes() == g_st.tobytes()
+    np.testing.assert_array_equal(q_dyn, q_st)
+    np.testing.assert_array_equal(s_dyn, s_st)
+    # outside the calibrated range: block scales saturate at 448, codes at 6
+    hot = inputs.gaussian(2, 32, 40.0, seed=8, stream="calib/hot")
+    q, s, _ = oracle.quantize_nvfp4(hot, global_scale=g)
+    rq, rs, _ = fr.quant_nv(hot.tolist(), 2, 32, global_in=Fr(float(g)))
+    np.testing.assert_array_equal(s, np.array(rs, np.uint8))
+    np.testing.assert_array_equal(_unpack_nibbles(q), np.array(rq, np.uint8))
+    assert (s == 126).any() and ((_unpack_nibbles(q) & 7) == 7).any()
