@@ -129,26 +129,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   const int vsc = lane * KS;
   // Every load stays inside its operand: a wave's 64 rows lie wholly inside or past
   // M (N); rows past the end, and stages after the last tile, read rows [0, 64).
-  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
+  // Part p (0..3) of a stage's DMA: code rows 16p..16p+15 of this wave's 64 for W
+  // and A, and one of the four scale loads (W d0, A d0, W d1, A d1).  The parts
+  // are issued a quarter of a phase apart so that the four waves' loads reach the
+  // texture unit spread out rather than in one burst.
+  auto dma_part = [&](int p, uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
     const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
     const bool vw = valid && rw0 < N, va = valid && ra0 < M;
     const int off_w = vw ? rw0 * KP + k0 / 2 : 0, off_a = va ? ra0 * KP + k0 / 2 : 0;
     const int off_sw = vw ? rw0 * KS + k0 / 16 : 0, off_sa = va ? ra0 * KS + k0 / 16 : 0;
     uint8_t* base = buf + wave * 64 * kRowB;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 16 * kRowB), 16, voff,
-                                               off_w + j * 16 * KP, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 16 * kRowB), 16, voff,
-                                               off_a + j * 16 * KP, 0, 0);
-    }
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + d * kTile + wave * 64), 4, vsc, off_sw + 4 * d,
-                                               0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + p * 16 * kRowB), 16, voff,
+                                             off_w + p * 16 * KP, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + p * 16 * kRowB), 16, voff,
+                                             off_a + p * 16 * KP, 0, 0);
+    const int d = p >> 1;
+    if (p & 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + (2 + d) * kTile + wave * 64), 4, vsc,
                                                off_sa + 4 * d, 0, 0);
-    }
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + d * kTile + wave * 64), 4, vsc,
+                                               off_sw + 4 * d, 0, 0);
+  };
+  auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dma_part(p, buf, sc, m0, n0, k0, valid);
   };
 
   const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
@@ -206,15 +211,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // 16 MFMAs, each followed by 4 of the next step's dequantization ops (and, for the
-  // first `reads` MFMAs, one LDS read; for the first `vmem` ones, one DMA load)
-  auto interleave = [&](int reads, int vmem) {
+  // 16 MFMAs, each followed by 4 of the next step's dequantization ops
+  // (and, for the first `reads` MFMAs, one LDS read; for MFMAs 0, 5 and 10 when
+  // `vmem`, one DMA load)
+  auto interleave = [&](int reads, bool vmem) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
       if (i < reads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < vmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (vmem && i % 5 == 0 && i < 15) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -269,36 +275,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     read_codes(c1w, c1a, cur, 1);
     mfma_step(acc, I0());
     dequant(I1(), I1(), c0w, c0a, s0w, s0a);
-    interleave(8, 0);
+    interleave(8, false);
     mfma_step(acc, I1());
     dequant(I0(), I2(), c0w, c0a, s0w, s0a);
-    interleave(0, 0);
+    interleave(0, false);
     mfma_step(acc, I0());
     dequant(I1(), I3(), c0w, c0a, s0w, s0a);
-    interleave(0, 0);
+    interleave(0, false);
     mfma_step(acc, I1());
     dequant(I0(), I0(), c1w, c1a, s1w, s1a);
-    interleave(0, 0);
+    interleave(0, false);
     // ---- B
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     __syncthreads();
     // ---- C
     read_scales(snxt);
     read_codes(c0w, c0a, nxt, 0);
-    dma_stage(cur, scur, dm0, dn0, dk0, dvalid);
+    dma_part(0, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I0());
     dequant(I1(), I1(), c1w, c1a, s1w, s1a);
-    interleave(16, 12);
+    interleave(16, true);
+    dma_part(1, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I1());
     dequant(I0(), I2(), c1w, c1a, s1w, s1a);
-    interleave(8, 0);
+    interleave(8, true);
+    dma_part(2, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I0());
     dequant(I1(), I3(), c1w, c1a, s1w, s1a);
-    interleave(0, 0);
+    interleave(0, true);
+    dma_part(3, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I1());
     convert_scales();
     dequant(I0(), I0(), c0w, c0a, s0w, s0a);
-    interleave(0, 0);
+    interleave(0, true);
   };
 
   int m0 = 0, n0 = 0, m0n = 0, n0n = 0;
