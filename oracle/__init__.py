@@ -57,6 +57,8 @@ def _load():
             "orc_quantize_mxfp8": (i32, [P, i64, i64, i32, P, P]),
             "orc_nvfp4_global_scale": (f32, [P, i64]),
             "orc_nvfp4_calibrate": (f32, [P, i64, f32]),
+            "orc_fp8_tensor_scale": (f32, [P, i64]),
+            "orc_quantize_fp8_tensor": (i32, [P, i64, i64, P, P, P]),
             "orc_quantize_nvfp4": (i32, [P, i64, i64, P, P, P, P]),
             "orc_dequant_mxfp8": (None, [P, P, i64, i32, P, i64, P]),
             "orc_dequant_nvfp4": (None, [P, P, f32, i64, P, i64, P]),
@@ -165,6 +167,26 @@ def quantize_nvfp4(x, global_scale=None):
     return q, s, np.float32(g_out[0])
 
 
+def fp8_tensor_scale(x) -> np.float32:
+    a = _as_u16(x)
+    return np.float32(_load().orc_fp8_tensor_scale(_ptr(a), a.size))
+
+
+def quantize_fp8_weight(x, scale=None):
+    """Weight-only FP8: bf16 [rows, cols] -> (E4M3 codes u8 [rows, cols], fp32
+    per-tensor decode scale).  scale None = RN_fp32(amax / 448)."""
+    a = _as_u16(x)
+    rows, cols = a.shape
+    q = np.empty((rows, cols), np.uint8)
+    s_out = np.zeros(1, np.float32)
+    s_in = None if scale is None else np.array([scale], np.float32)
+    rc = _load().orc_quantize_fp8_tensor(_ptr(a), rows, cols, None if s_in is None else _ptr(s_in), _ptr(q),
+                                         _ptr(s_out))
+    if rc != 0:
+        raise ValueError("orc_quantize_fp8_tensor: bad arguments (rc=%d)" % rc)
+    return q, np.float32(s_out[0])
+
+
 # -------------------------------------------------------------- dequant / GEMM
 
 def _rows(row_idx, n_all):
@@ -219,6 +241,31 @@ def gemm_mxfp8(a_q, a_s, w_q, w_s, a_fmt=E4M3, w_fmt=E4M3, bias=None, epi=EPI_NO
     a = dequant_mxfp8(a_q, a_s, a_fmt, row_idx)
     w = dequant_mxfp8(w_q, w_s, w_fmt)
     return linear(a, w, 1.0, bias, epi)
+
+
+_TABLES = {}
+
+
+def _table(name):
+    """Decoded value of every bf16 bit pattern / every E4M3 code (fp64)."""
+    if name not in _TABLES:
+        if name == "bf16":
+            _TABLES[name] = np.array([bf16_value(b) for b in range(65536)], np.float64)
+        else:
+            _TABLES[name] = np.array([code_value(E4M3, c) if (c & 0x7F) != 0x7F else np.nan for c in range(256)],
+                                     np.float64)
+    return _TABLES[name]
+
+
+def gemm_bf16_fp8w(a_bits, w_q, w_scale, bias=None, epi=EPI_NONE, row_idx=None):
+    """Weight-only FP8 linear: r = epi(s_w * A . val(W)^T + bias) in fp64, with A
+    the exact bf16 values and W the E4M3 values (s_w applied once, like alpha)."""
+    a = _as_u16(a_bits)
+    if row_idx is not None:
+        a = a[np.asarray(row_idx)]
+    a_deq = _table("bf16")[a]
+    w_deq = _table("e4m3")[np.asarray(w_q, np.uint8)]
+    return linear(a_deq, w_deq, float(w_scale), bias, epi)
 
 
 def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=EPI_NONE, row_idx=None):

@@ -232,6 +232,38 @@ float orc_nvfp4_global_scale(const uint16_t* x, int64_t n) {
     return orc_rn_fp32_div(amax, 6.0 * 448.0);
 }
 
+/* Weight-only FP8 (page "麦橘超然性能实战分析：float8量化如何提升GPU利用率",
+ * section 3.2: the DiT weights are loaded as float8_e4m3fn while activations stay
+ * bf16, and section 4 / page "FP8量化技术提升SD3.5在低带宽环境下的响应速度", step 2:
+ * q = round(w / scale), dequantized as q * scale; the product runs in bf16).
+ * Per-tensor decode scale s = RN_fp32(amax / 448) (1 for an all-zero tensor) or
+ * the given one; q = RN_E4M3,sat(w / s), sign copied. */
+float orc_fp8_tensor_scale(const uint16_t* x, int64_t n) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) amax = fmax(amax, fabs(orc_bf16_value(x[i])));
+    if (amax == 0.0) return 1.0f;
+    return orc_rn_fp32_div(amax, 448.0);
+}
+
+int orc_quantize_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols, const float* scale_in,
+                            uint8_t* q, float* scale_out) {
+    const float s = scale_in ? *scale_in : orc_fp8_tensor_scale(x, rows * cols);
+    if (!(s > 0.0f) || !isfinite(s)) return -2;
+    *scale_out = s;
+    double v43[128];
+    const int n43 = finite_table(ORC_E4M3, v43);
+    const double sd = (double)s;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint16_t b = x[r * cols + c];
+            const int mag = round_in_table(v43, n43, fabs(orc_bf16_value(b)), sd);
+            q[r * cols + c] = (uint8_t)(mag | (((b >> 15) & 1) << 7));
+        }
+    }
+    return 0;
+}
+
 /* Static-scale calibration (page "FP8量化技术提升SD3.5在低带宽环境下的响应速度",
  * step 1: record each layer's maximum over a calibration batch and set the scale
  * so that nothing is truncated).  Folds one calibration tensor into the running

@@ -127,3 +127,20 @@ def quant_nv(x_bits, rows: int, cols: int, global_in=None):
                 mag = 0 if S == 0 else rne_sat(abs(vals[i]) / (S * sg), E2M1)
                 q[r][b * 16 + i] = mag | (0x8 if blk[i] & 0x8000 else 0)
     return q, s, sg
+
+
+def quant_fp8_tensor(x_bits, rows: int, cols: int, scale=None):
+    """Weight-only FP8: s = RN_fp32(amax / 448) (1 for an all-zero tensor) or the
+    given scale; q = RN_E4M3,sat(x / s) with the input's sign bit."""
+    allv = [bf16_value(x_bits[r][c]) for r in range(rows) for c in range(cols)]
+    if scale is None:
+        amax = max(abs(v) for v in allv)
+        s = Fr(1) if amax == 0 else rn_fp32(amax / 448)
+    else:
+        s = Fr(scale)
+    q = [[0] * cols for _ in range(rows)]
+    for r in range(rows):
+        for c in range(cols):
+            b = x_bits[r][c]
+            q[r][c] = rne_sat(abs(bf16_value(b)) / s, E4M3) | (0x80 if b & 0x8000 else 0)
+    return q, s

@@ -404,3 +404,46 @@ def test_calibrated_scale_pins():
     np.testing.assert_array_equal(s, np.array(rs, np.uint8))
     np.testing.assert_array_equal(_unpack_nibbles(q), np.array(rq, np.uint8))
     assert (s == 126).any() and ((_unpack_nibbles(q) & 7) == 7).any()
+
+
+# ------------------------------------ weight-only FP8 (NEXT-2 row, P4 3.2, P5)
+
+def test_fp8_weight_quantizer_against_rationals():
+    """Per-tensor FP8 weights: codes and the decode scale against exact rational
+    rounding -- dynamic scale, a power-of-two static scale that puts values on
+    E4M3 midpoints (ties), and a small static scale that saturates."""
+    w = inputs.weight(6, 48, seed=3, stream="w8/pin")
+    q, s = oracle.quantize_fp8_weight(w)
+    rq, rs = fr.quant_fp8_tensor(w.tolist(), 6, 48)
+    assert Fr(float(s)) == rs
+    np.testing.assert_array_equal(q, np.array(rq, np.uint8))
+    ties = _bits([[17.0, 19.0, 21.0, -23.0, 0.0, -0.0, 1e-3, 460.0, 2.25 * 2 ** -7, 500.0, -9.0, 13.0]])
+    for sc in (1.0, 0.5, 2.0 ** -4):
+        q, s = oracle.quantize_fp8_weight(ties, scale=sc)
+        rq, _ = fr.quant_fp8_tensor(ties.tolist(), 1, ties.shape[1], scale=Fr(sc))
+        np.testing.assert_array_equal(q, np.array(rq, np.uint8))
+    q, _ = oracle.quantize_fp8_weight(ties, scale=1.0)
+    assert q[0, 0] == 0x58 and q[0, 1] == 0x5A          # 17 -> 16 (even), 19 -> 20 (even)
+    assert q[0, 7] == 0x7E and q[0, 9] == 0x7E          # 460, 500 saturate to 448
+
+
+def test_fp8_weight_worked_example():
+    """The pages' worked example: 0.176 with scale 0.01 maps to 18 (E4M3 0x59),
+    dequantizing to 0.18."""
+    w = _bits([[0.176]])
+    q, s = oracle.quantize_fp8_weight(w, scale=0.01)
+    assert q[0, 0] == 0x59 and oracle.code_value(oracle.E4M3, int(q[0, 0])) == 18.0
+    assert abs(18.0 * float(s) - 0.18) < 1e-8
+
+
+def test_fp8_weight_gemm_textbook():
+    """Scale 1 and integer-valued weights and activations: the weight-only FP8
+    linear equals the integer matrix product exactly."""
+    rng = np.random.RandomState(4)
+    a_int = rng.randint(-8, 9, size=(5, 64))
+    w_int = rng.randint(-15, 16, size=(7, 64))
+    a = _bits(a_int.astype(np.float64))
+    w = _bits(w_int.astype(np.float64))
+    q, s = oracle.quantize_fp8_weight(w, scale=1.0)
+    r = oracle.gemm_bf16_fp8w(a, q, s)
+    np.testing.assert_array_equal(r, (a_int @ w_int.T).astype(np.float64))
