@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 METRIC = "block-scaled GEMM TFLOP/s at FLUX shapes (% MFMA peak); quantizer GB/s (% HBM)"
 # MI355X published peaks (dense): HBM3E 8 TB/s; MFMA fp8 5.0 PF, fp4 10.1 PF, fp16/bf16 2.5 PF
 PEAK_HBM_GBPS = 8000.0
-PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp16": 2500.0}
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "fp16": 2500.0, "bf16": 2500.0}
+PEAK_BF16_TFLOPS = PEAK_TFLOPS["bf16"]
 
 MX_LINEARS = [  # name, N, K, epilogue   (M = 4608)
     ("qkv", 9216, 3072, "none"),
@@ -202,6 +203,42 @@ def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
             "static_ms": round(res["static"], 4), "dynamic_ms": round(res["dynamic"], 4),
             "static_GB/s": round(rate, 1), "static_frac_of_hbm": round(rate / PEAK_HBM_GBPS, 4),
             "calibrated_scale": float(running[0])}
+    return out
+
+
+def weight_only_fp8_variant(torch, mxq, inputs, wl, reps: int = 20):
+    """Weight-only FP8 on the double-stream linears: per-tensor E4M3 weights (quantized
+    once, timed separately), the step's bf16 activations taken as they are, the same
+    epilogues.  torch's bf16 GEMM on the same shapes is timed beside it for context."""
+    out = {"weights": "per-tensor E4M3, dynamic scale from the weight's amax",
+           "peak_TFLOP/s": PEAK_BF16_TFLOPS}
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(3):
+            f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    for L in wl.mx:
+        w = inputs.to_torch(inputs.weight(L["N"], L["K"], seed=0, stream="bench/%s/W" % L["name"]), "cuda")
+        q_ms = timed(lambda: mxq.quantize_fp8_weight(w))
+        wq, ws = mxq.quantize_fp8_weight(w)
+        c = torch.empty((M_MX, L["N"]), dtype=torch.bfloat16, device="cuda")
+        g_ms = timed(lambda: mxq.gemm_bf16_fp8w(L["x"], wq, ws, bias=L["b"], epi=L["epi"], out=c))
+        t_ms = timed(lambda: torch.matmul(L["x"], w.t()))
+        flops = 2 * M_MX * L["N"] * L["K"]
+        rate = flops / (g_ms * 1e-3) / 1e12
+        out["gemm_bf16_fp8w_" + L["name"]] = {
+            "shape": [M_MX, L["N"], L["K"]], "epi": L["epi"], "ms": round(g_ms, 4), "TFLOP/s": round(rate, 1),
+            "frac": round(rate / PEAK_BF16_TFLOPS, 4), "torch_bf16_ms": round(t_ms, 4),
+            "quantize_weight_ms": round(q_ms, 4)}
+        del w, wq, ws, c
     return out
 
 
@@ -380,6 +417,7 @@ def main():
         "roofline": roofline,
     }
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
+    result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)

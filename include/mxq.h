@@ -146,6 +146,38 @@ mxq_status mxq_nvfp4_calibrate(const void* x, int64_t rows, int64_t cols, float*
                                void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Weight-only FP8: per-tensor E4M3 weights [P4 section 3.2: the DiT weights are
+ * held as float8_e4m3fn while activations stay bf16; P5 step 2: q = round(w/scale),
+ * dequantized as q * scale].
+ *   w         : bf16 [rows, cols], device (a weight, N x K).
+ *   rows, cols: > 0, cols a multiple of 16.
+ *   scale_in  : device fp32 decode scale to use (positive, finite), or NULL for
+ *               s = RN_fp32(amax(w) / 448) (1 for an all-zero tensor).
+ *   q         : u8 [rows, cols] E4M3 codes, device, written: RN_E4M3_sat(w / s),
+ *               sign copied.
+ *   scale_out : device fp32, written with the s used.
+ *   workspace : NULL mode only; size and rules as for mxq_quantize_nvfp4.
+ */
+mxq_status mxq_quantize_fp8_weight(const void* w, int64_t rows, int64_t cols, const float* scale_in,
+                                   void* q, float* scale_out, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
+/*
+ * Weight-only FP8 GEMM [P4 sections 3.2 and 4: FP8 weights converted back for a
+ * bf16 product ("fake quantization", P5), at a small time cost].
+ *   C[m, n] = epi( s_w sum_k a[m,k] val(w_q[n,k]) (+ bias[n]) ), fp32 accumulation,
+ *   one RNE to bf16.  The E4M3 values are exact in bf16, so the products are exact.
+ *   a      : bf16 [M, K] row-major, device.
+ *   w_q    : u8 [N, K] E4M3 (from mxq_quantize_fp8_weight), device.
+ *   w_scale: device fp32 s_w.
+ *   M, N, K, bias, epi, c, errors: as mxq_gemm_mxfp8 (a counts 2 bytes per
+ *   element towards the 2 GiB operand limit).
+ */
+mxq_status mxq_gemm_bf16_fp8w(const void* a, const void* w_q, const float* w_scale, int64_t M,
+                              int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c,
+                              void* stream);
+
+/*
  * MXFP8 block-scaled GEMM [P3: every nn.Linear runs quantized; P2 §5.2: 128 alignment].
  *   C[m, n] = epi( sum_k val(a_q[m,k]) 2^(a_s[m,k/32]-127) val(w_q[n,k]) 2^(w_s[n,k/32]-127)
  *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.

@@ -18,7 +18,8 @@ import threading
 
 __all__ = [
     "load", "MXQError", "E4M3", "E5M2", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
-    "quantize_mxfp8", "quantize_nvfp4", "nvfp4_workspace_size", "nvfp4_calibrate", "gemm_mxfp8", "gemm_nvfp4",
+    "quantize_mxfp8", "quantize_nvfp4", "nvfp4_workspace_size", "nvfp4_calibrate", "quantize_fp8_weight",
+    "gemm_mxfp8", "gemm_nvfp4", "gemm_bf16_fp8w",
     "library_path",
 ]
 
@@ -33,7 +34,8 @@ _lock = threading.Lock()
 _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
-           "mxq_nvfp4_calibrate", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_status_string", "mxq_last_error"]
+           "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4",
+           "mxq_gemm_bf16_fp8w", "mxq_status_string", "mxq_last_error"]
 
 
 class MXQError(RuntimeError):
@@ -64,14 +66,16 @@ def load():
         lib.mxq_quantize_nvfp4_workspace_size.restype = sz
         lib.mxq_quantize_nvfp4.argtypes = [P, i64, i64, P, P, P, P, P, sz, P]
         lib.mxq_nvfp4_calibrate.argtypes = [P, i64, i64, P, P, sz, P]
+        lib.mxq_quantize_fp8_weight.argtypes = [P, i64, i64, P, P, P, P, sz, P]
+        lib.mxq_gemm_bf16_fp8w.argtypes = [P, P, P, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P]
         lib.mxq_status_string.argtypes = [i32]
         lib.mxq_status_string.restype = ctypes.c_char_p
         lib.mxq_last_error.argtypes = []
         lib.mxq_last_error.restype = ctypes.c_char_p
-        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_nvfp4_calibrate", "mxq_gemm_mxfp8",
-                  "mxq_gemm_nvfp4"):
+        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight",
+                  "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w"):
             getattr(lib, f).restype = i32
         _lib = lib
         return lib
@@ -185,6 +189,33 @@ def nvfp4_calibrate(x, running=None, workspace=None, stream=None):
     return running
 
 
+def quantize_fp8_weight(w, scale=None, out=None, workspace=None, stream=None):
+    """Weight-only FP8: bf16 [R, C] -> (E4M3 codes uint8 [R, C], fp32 [1] decode
+    scale).  scale: None (RN_fp32(amax / 448)) or a 1-element fp32 CUDA tensor."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    R, C = w.shape
+    if scale is not None:
+        _need(scale, torch.float32, "scale", w.device)
+    if out is not None:
+        q, s = out
+    else:
+        q = torch.empty((R, C), dtype=torch.uint8, device=w.device)
+        s = torch.empty((1,), dtype=torch.float32, device=w.device)
+    ws_bytes = 0
+    if scale is None:
+        ws_bytes = nvfp4_workspace_size(R, C)
+        if workspace is None:
+            workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=w.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.mxq_quantize_fp8_weight(_ptr(w), R, C, _ptr(scale), _ptr(q), _ptr(s), _ptr(workspace), ws_bytes,
+                                       _stream(stream)))
+    return q, s
+
+
 # ------------------------------------------------------------------------ GEMMs
 
 def _epi(epi, bias):
@@ -236,4 +267,26 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, stre
     lib = load()
     _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
                               M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
+    return c
+
+
+def gemm_bf16_fp8w(a, w_q, w_scale, bias=None, epi=None, out=None, stream=None):
+    """Weight-only FP8: C[M, N] = epi(s_w A . val(W)^T) in bf16, A bf16 [M, K], W E4M3 [N, K]."""
+    torch = _torch()
+    _need(a, torch.bfloat16, "a")
+    _need(w_q, torch.uint8, "w_q")
+    _need(w_scale, torch.float32, "w_scale")
+    M, K = a.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K:
+        raise ValueError("operand shapes disagree")
+    if epi is None:
+        epi = "none" if bias is None else "bias"
+    e = _epi(epi, bias)
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    lib = load()
+    _check(lib.mxq_gemm_bf16_fp8w(_ptr(a), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(bias), e, _ptr(c),
+                                  _stream(stream)))
     return c

@@ -141,6 +141,29 @@ mxq_status mxq_nvfp4_calibrate(const void* x, int64_t rows, int64_t cols, float*
                   "mxq_nvfp4_calibrate launch");
 }
 
+mxq_status mxq_quantize_fp8_weight(const void* w, int64_t rows, int64_t cols, const float* scale_in, void* q,
+                                   float* scale_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!w || !q || !scale_out) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  if (rows <= 0 || cols <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "rows and cols must be positive");
+  if (cols % 16 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (rows > INT64_MAX / cols) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "rows * cols overflows");
+  if (!aligned16(w) || !aligned16(q)) return fail(MXQ_ERROR_MISALIGNED, "w and q must be 16-byte aligned");
+  if (((uintptr_t)scale_out & 3u) || ((uintptr_t)scale_in & 3u))
+    return fail(MXQ_ERROR_MISALIGNED, "scale pointers must be 4-byte aligned");
+  if (!scale_in) {
+    const size_t need = mxq_quantize_nvfp4_workspace_size(rows, cols);
+    if (!workspace || ws_bytes < need)
+      return fail(MXQ_ERROR_WORKSPACE, "dynamic mode needs a %zu-byte workspace (got %zu)", need,
+                  workspace ? ws_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 3u) return fail(MXQ_ERROR_MISALIGNED, "workspace must be 4-byte aligned");
+  }
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_quantize_fp8_tensor(w, rows * cols, scale_in, q, scale_out, (uint32_t*)workspace,
+                                                  (hipStream_t)stream),
+                  "mxq_quantize_fp8_weight launch");
+}
+
 static mxq_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c,
                                     int64_t a_row_bytes_num, int64_t a_row_bytes_den) {
   if (!c) return fail(MXQ_ERROR_INVALID_VALUE, "null output pointer");
@@ -158,6 +181,19 @@ static mxq_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void*
   if (!aligned16(c) || (bias && !aligned16(bias)))
     return fail(MXQ_ERROR_MISALIGNED, "c and bias must be 16-byte aligned");
   return MXQ_SUCCESS;
+}
+
+mxq_status mxq_gemm_bf16_fp8w(const void* a, const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                              const void* bias, mxq_epilogue epi, void* c, void* stream) {
+  if (!a || !w_q || !w_scale) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  mxq_status s = check_gemm_common(M, N, K, bias, epi, c, 2, 1);
+  if (s != MXQ_SUCCESS) return s;
+  if (!aligned16(a) || !aligned16(w_q)) return fail(MXQ_ERROR_MISALIGNED, "operands must be 16-byte aligned");
+  if ((uintptr_t)w_scale & 3u) return fail(MXQ_ERROR_MISALIGNED, "w_scale must be 4-byte aligned");
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_gemm_w8(a, w_q, w_scale, M, N, K, bias, (int)epi, c, (hipStream_t)stream),
+                  "mxq_gemm_bf16_fp8w launch");
 }
 
 mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_kind, const void* w_q,

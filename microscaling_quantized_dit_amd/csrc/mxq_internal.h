@@ -23,6 +23,13 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
 hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running, uint32_t* partials,
                                   hipStream_t stream);
 
+// Per-tensor E4M3 weights: scale_in NULL = RN_fp32(amax / 448) via the partials.
+hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const float* scale_in, void* q,
+                                     float* scale_out, uint32_t* partials, hipStream_t stream);
+
+hipError_t launch_gemm_w8(const void* a, const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                          const void* bias, int epi, void* c, hipStream_t stream);
+
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q,
                              const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
                              const void* bias, int epi, void* c, hipStream_t stream);
@@ -76,6 +83,97 @@ __device__ __forceinline__ float gelu_tanh(float y) {
   const float m2log2e = -2.0f * 1.4426950408889634f; // -2 log2(e)
   const float u = k0 * (y + k1 * y * y * y);
   return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+}
+
+// s_waitcnt immediate for vmcnt = vm (0..63) and lgkmcnt = lgkm (0..15), expcnt
+// left open.  vmcnt counts vector loads (LDS DMA included) and stores alike, and
+// loads and stores may retire out of order with respect to each other.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+constexpr int kWaitLgkm = waitcnt_imm(63, 0);   // LDS reads only
+constexpr int kWaitAll = waitcnt_imm(0, 0);     // vector memory and LDS reads
+constexpr int kWaitVm = waitcnt_imm(0, 15);     // vector memory only
+
+// Workgroup barrier without the memory fences of __syncthreads(): those make the
+// compiler wait for every vector memory operation in flight, epilogue stores
+// included.  The caller's s_waitcnt retires the LDS writes (DMA or ds_write) that
+// the barrier publishes; the signal fences keep the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Bytes of LDS one wave needs to stage its output for epilogue_block<.., W, ..>.
+constexpr int epilogue_lds_bytes(int W) { return 32 * (2 * W + 16); }
+
+// The tile's bias for one wave's 128 columns [n, n + 128) -> bias_w in LDS (one
+// 1 KiB DMA, of which the first 256 bytes are used; reads past the end of the bias
+// return zeros).  Retired by the next vmcnt(0); the wave's own epilogue reads it.
+__device__ __forceinline__ void load_bias(__amdgpu_buffer_rsrc_t rb, uint8_t* bias_w, int n, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)bias_w, 16, lane * 16, n * 2, 0, 0);
+}
+
+// Epilogue of one wave's 128 x 128 block of a 32x32-MFMA GEMM, whose lane l holds
+// in acc[i][j][v] the result for row 32j + l % 32 and column
+// 32i + 8(v / 4) + 4(l / 32) + v % 4 of the block:
+//   C[m_base + row][n_base + col] = bf16(epi(alpha * acc + bias[col]))
+// (alpha applied when SCALE).  The block goes out 32 rows and W (128 or 64)
+// columns at a time through `stage` (epilogue_lds_bytes(W) of this wave's LDS):
+// each lane writes its values there, then reads 16 bytes of a row back, so that
+// every global store covers whole row segments of 2W bytes instead of 32 rows of
+// 16 bytes.  A wave's LDS accesses complete in order, so no barrier is needed.
+template <int EPI, int W, bool SCALE>
+__device__ __forceinline__ void epilogue_block(const v16f_t (&acc)[4][4], float alpha, const uint8_t* bias_w,
+                                               uint8_t* stage, uint16_t* c, int N, int m_base, int n_base,
+                                               int lane) {
+  constexpr int kRow = 2 * W + 16;            // staged row bytes (+16 against bank conflicts)
+  constexpr int kLanesPerRow = 2 * W / 16;    // 16-byte chunks per staged row
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  const int r = lane & 31, g = lane >> 5;
+  const int srow = lane / kLanesPerRow, chunk = lane % kLanesPerRow;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int h = 0; h < 128 / W; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < W / 32; ++ii) {
+        const int i = h * (W / 32) + ii;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = 32 * i + 8 * qd + 4 * g;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = SCALE ? alpha * acc[i][j][4 * qd + e] : acc[i][j][4 * qd + e];
+          if (EPI >= 1) {
+            const uint2 b = *(const uint2*)(bias_w + 2 * col);
+            y[0] += bf16_lo(b.x);
+            y[1] += bf16_hi(b.x);
+            y[2] += bf16_lo(b.y);
+            y[3] += bf16_hi(b.y);
+          }
+          if (EPI == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = gelu_tanh(y[e]);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(y[0], y[1]);
+          o.y = pack_bf16x2(y[2], y[3]);
+          *(uint2*)(stage + r * kRow + 2 * (col - h * W)) = o;
+        }
+      }
+      uint16_t* cb = c + (size_t)(m_base + 32 * j) * N + n_base + h * W + 8 * chunk;
+#pragma unroll
+      for (int q = 0; q < 32 / kRowsPerStore; ++q) {
+        const int row = kRowsPerStore * q + srow;
+        const uint4 v = *(const uint4*)(stage + row * kRow + 16 * chunk);
+        *(uint4*)(cb + (size_t)row * N) = v;
+      }
+    }
+  }
 }
 
 // Remap a linear workgroup id so that ids placed round-robin on the 8 XCDs

@@ -250,6 +250,89 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   }
 }
 
+// Per-tensor FP8 weights (page "麦橘超然性能实战分析：float8量化如何提升GPU利用率",
+// section 3.2: DiT weights held as float8_e4m3fn; page "FP8量化技术提升SD3.5在低带宽
+// 环境下的响应速度", step 2: q = round(w / scale)):
+//   s = RN_fp32(amax / 448) (1 for an all-zero tensor; or given), q = RN_E4M3_sat(w / s).
+// Eight values per lane (one uint4 of bf16 -> one uint2 of codes).  The quotient is
+// bracketed like the NVFP4 codes; a near tie is settled by round_up_at against the
+// midpoint of the two candidate codes; an extreme s takes the fp64 search.
+__global__ __launch_bounds__(kThreads) void k_quant_fp8_tensor(const uint4* __restrict__ x, int64_t n_chunks,
+                                                               const float* __restrict__ scale_in,
+                                                               const uint32_t* __restrict__ partials,
+                                                               int n_partials, uint2* __restrict__ q,
+                                                               float* __restrict__ scale_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int t = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll);
+  uint4 v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + u * kThreads + t;
+    v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+  }
+  float sw;
+  if (scale_in) {
+    sw = *scale_in;
+  } else {
+    uint32_t m = t < n_partials ? partials[t] : 0u;
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    const uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    sw = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 448.0f;   // IEEE division
+  }
+  if (blockIdx.x == 0 && t == 0) *scale_out = sw;
+  const double rd = 1.0 / (double)sw;
+  const float r_lo = (float)(rd * (1.0 - 0x1p-19)), r_hi = (float)(rd * (1.0 + 0x1p-19));
+  // fp32 brackets and the two-product test need sw and 1/sw well inside fp32's range
+  const bool fast = rd < 0x1p126 && rd > 0x1p-126 && sw >= 0x1p-100f;
+
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t c = base + u * kThreads + t;
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // four values -> four codes, for each bracket
+      int lo = 0, hi = 0;
+      float xs[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = (e & 1) ? dev::bf16_hi(w[2 * h + (e >> 1)]) : dev::bf16_lo(w[2 * h + (e >> 1)]);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * r_lo, -448.0f, 448.0f),
+                                           __builtin_amdgcn_fmed3f(xs[1] * r_lo, -448.0f, 448.0f), lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * r_lo, -448.0f, 448.0f),
+                                           __builtin_amdgcn_fmed3f(xs[3] * r_lo, -448.0f, 448.0f), lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * r_hi, -448.0f, 448.0f),
+                                           __builtin_amdgcn_fmed3f(xs[1] * r_hi, -448.0f, 448.0f), hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * r_hi, -448.0f, 448.0f),
+                                           __builtin_amdgcn_fmed3f(xs[3] * r_hi, -448.0f, 448.0f), hi, true);
+      uint32_t codes = (uint32_t)lo;
+      if (__builtin_expect(!fast, 0)) {
+        codes = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t mag = (uint32_t)exact_block_scale((double)fabsf(xs[e]), (double)sw);
+          codes |= (mag | (__float_as_uint(xs[e]) >> 31 << 7)) << (8 * e);
+        }
+      } else if (__builtin_expect(codes != (uint32_t)hi, 0)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t cl = (codes >> (8 * e)) & 0x7Fu, ch = ((uint32_t)hi >> (8 * e)) & 0x7Fu;
+          if (cl != ch) {
+            const float mk = (__builtin_amdgcn_cvt_f32_fp8((int)cl, 0) + __builtin_amdgcn_cvt_f32_fp8((int)ch, 0)) * 0.5f;
+            const uint32_t mag = round_up_at(fabsf(xs[e]), mk, sw, (ch & 1) == 0) ? ch : cl;
+            codes = (codes & ~(0x7Fu << (8 * e))) | (mag << (8 * e));
+          }
+        }
+      }
+      out[h] = codes;
+    }
+    if (c < n_chunks) q[c] = make_uint2(out[0], out[1]);
+  }
+}
+
 // Calibration fold: running = max(running, RN_fp32(amax / 2688)) over the partial
 // maxima of one calibration tensor (an all-zero tensor contributes 0).  One
 // workgroup; the caller orders calls on one stream.
@@ -269,6 +352,25 @@ __global__ __launch_bounds__(kThreads) void k_calib_fold(const uint32_t* __restr
 }
 
 }  // namespace
+
+hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const float* scale_in, void* q,
+                                     float* scale_out, uint32_t* partials, hipStream_t stream) {
+  const int64_t n_chunks = n_elems / 8;
+  int n_partials = 0;
+  if (!scale_in) {
+    n_partials = nvfp4_amax_partials(n_elems);
+    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x, n_chunks,
+                       partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_fp8_tensor, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x, n_chunks,
+                     scale_in, partials, n_partials, (uint2*)q, scale_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running, uint32_t* partials,
                                   hipStream_t stream) {

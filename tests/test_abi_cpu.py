@@ -106,6 +106,32 @@ def test_nvfp4_calibrate_validation(lib):
     assert call(wsb=need - 4) == WORKSPACE
 
 
+def test_fp8_weight_validation(lib):
+    need = lib.mxq_quantize_nvfp4_workspace_size(4, 64)
+
+    def quant(w=FAKE, rows=4, cols=64, sin=None, q=FAKE2, sout=FAKE, ws=FAKE2, wsb=need):
+        return lib.mxq_quantize_fp8_weight(w, rows, cols, sin, q, sout, ws, wsb, None)
+
+    assert quant(w=None) == INVALID
+    assert quant(sout=None) == INVALID
+    assert quant(cols=24) == SHAPE
+    assert quant(q=MIS) == MISALIGNED
+    assert quant(sout=FAKE + 2) == MISALIGNED
+    assert quant(ws=None) == WORKSPACE
+    assert quant(sin=FAKE, ws=None) == DEVICE          # static mode needs no workspace; no GPU here
+
+    def gemm(a=FAKE, w=FAKE2, s=FAKE, M=128, N=256, K=256, bias=None, epi=0, c=FAKE):
+        return lib.mxq_gemm_bf16_fp8w(a, w, s, M, N, K, bias, epi, c, None)
+
+    assert gemm(s=None) == INVALID
+    assert gemm(K=192) == SHAPE
+    assert gemm(epi=1) == INVALID
+    assert gemm(a=MIS) == MISALIGNED
+    assert gemm(s=FAKE + 2) == MISALIGNED
+    assert gemm(M=1 << 20, K=1024) == SHAPE              # A > 2 GiB at 2 bytes per element
+    assert gemm() == DEVICE
+
+
 def _g8(lib, M=128, N=256, K=256, bias=None, epi=0, c=FAKE, a=FAKE, ak=0, wk=0):
     return lib.mxq_gemm_mxfp8(a, FAKE2, ak, FAKE, FAKE2, wk, M, N, K, bias, epi, c, None)
 

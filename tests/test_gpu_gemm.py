@@ -220,3 +220,53 @@ def test_long_sequence(mxq, N):
     for fmt in (oracle.E4M3, oracle.E5M2):
         _assert_close(*run_mx(mxq, MX(a, fmt), MX(w, fmt), bias=b, epi="bias", rows=rows), "cfg5 mx %d" % fmt)
     _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias", rows=rows), "cfg5 nv")
+
+
+# ---------------------------------------------- weight-only FP8 (bf16 x E4M3)
+
+def run_w8(mxq, a, w_bits, bias=None, epi="none", rows=None, scale=None):
+    import torch
+    q, s = oracle.quantize_fp8_weight(w_bits, scale=scale)
+    c = mxq.gemm_bf16_fp8w(inputs.to_torch(a, "cuda"), _t(q), _t(np.array([s], np.float32)),
+                           bias=None if bias is None else inputs.to_torch(bias, "cuda"), epi=epi)
+    g = _bf16_out(c)
+    r = oracle.gemm_bf16_fp8w(a, q, s, bias=bias, epi=EPIS[epi], row_idx=rows)
+    return (g if rows is None else g[rows]), r
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 640, 256), (640, 384, 1152), (2432, 7808, 256)])
+def test_w8_shapes(mxq, M, N, K):
+    """Weight-only FP8 GEMM: ragged 256-tiles, odd stage counts, more tiles than CUs."""
+    a = inputs.flux_activation(M, K, seed=M, stream="w8/A")
+    w = inputs.weight(N, K, seed=N, stream="w8/W")
+    _assert_close(*run_w8(mxq, a, w), "w8 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("epi", ["bias", "bias_gelu"])
+def test_w8_epilogues_and_scales(mxq, epi):
+    a = inputs.flux_activation(256, 512, seed=3, stream="w8e/A")
+    w = inputs.weight(384, 512, seed=3, stream="w8e/W")
+    b = inputs.bias(384, 512, seed=3, stream="w8e/b")
+    _assert_close(*run_w8(mxq, a, w, bias=b, epi=epi), "w8 " + epi)
+    _assert_close(*run_w8(mxq, a, w, scale=2.0 ** -7), "w8 static scale")
+
+
+def test_w8_integer_products_exact(mxq):
+    """Scale 1, integer activations and weights: the bf16 output equals the
+    integer product (|C| < 256, exact in bf16)."""
+    rng = np.random.RandomState(11)
+    a_int = rng.randint(-2, 3, size=(256, 256))
+    w_int = rng.randint(-2, 3, size=(256, 256))
+    g, r = run_w8(mxq, inputs.bf16_bits(a_int.astype(np.float64)), inputs.bf16_bits(w_int.astype(np.float64)),
+                  scale=1.0)
+    np.testing.assert_array_equal(g, r)
+
+
+@pytest.mark.parametrize("name,N,K", [("qkv", 9216, 3072), ("mlp_down", 3072, 12288)])
+def test_w8_flux_shapes(mxq, name, N, K):
+    """FLUX double-stream linears at M = 4608 with bf16 activations and E4M3
+    weights; 64 sampled rows."""
+    M = 4608
+    a = inputs.flux_activation(M, K, seed=0, stream="w8f/%s/A" % name)
+    w = inputs.weight(N, K, seed=0, stream="w8f/%s/W" % name)
+    _assert_close(*run_w8(mxq, a, w, rows=_rows(M, 64, 5)), "w8 " + name)

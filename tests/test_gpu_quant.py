@@ -188,3 +188,32 @@ def test_nvfp4_static_calibration(mxq):
     # a running scale that already exceeds the tensor's stays put
     r = torch.tensor([1e3], dtype=torch.float32, device="cuda")
     assert float(mxq.nvfp4_calibrate(_dev(batches[0]), r)[0]) == 1e3
+
+
+# --------------------------------------------- weight-only FP8 (per-tensor E4M3)
+
+def _check_w8(mxq, bits, static=None):
+    import torch
+    sin = None if static is None else torch.tensor([static], dtype=torch.float32, device="cuda")
+    q, s = mxq.quantize_fp8_weight(_dev(bits), scale=sin)
+    q, s = _np(q), np.float32(_np(s)[0])
+    rq, rs = oracle.quantize_fp8_weight(bits, scale=static)
+    assert s.tobytes() == np.float32(rs).tobytes()
+    np.testing.assert_array_equal(q, rq)
+
+
+def test_fp8_weight_quantizer(mxq):
+    """Per-tensor E4M3 weights bit-exact to the oracle: FLUX weight shapes, every
+    finite bf16 pattern under three scales, ties and saturation, extreme scales."""
+    _check_w8(mxq, inputs.weight(3072, 3072, seed=0, stream="w8/W"))
+    _check_w8(mxq, inputs.weight(1024, 12288, seed=1, stream="w8/W2"), static=2.0 ** -9)
+    sweep = _sweep(16, [0x3F80, 0x4B00, 0x0080])
+    _check_w8(mxq, sweep)
+    _check_w8(mxq, sweep, static=1.0)
+    _check_w8(mxq, sweep, static=0.01)
+    _check_w8(mxq, sweep, static=2.0 ** -110)            # outside the fp32 bracket range: exact path
+    ties = inputs.bf16_bits(np.array([[17.0, 19.0, 21.0, -23.0, 0.0, -0.0, 1e-3, 460.0,
+                                       2.25 * 2 ** -7, 500.0, -9.0, 13.0, 448.0, -0.015625, 3.0, 1e-30]]))
+    for sc in (1.0, 0.5, 2.0 ** -4, 3.0):
+        _check_w8(mxq, np.tile(ties, (2, 2)), static=sc)
+    _check_w8(mxq, np.zeros((2, 32), np.uint16))         # all-zero: scale 1
