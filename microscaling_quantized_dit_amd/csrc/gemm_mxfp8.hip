@@ -26,6 +26,8 @@
 // tiles as one stream of stages, so the next tile's first stages are in flight
 // during the previous tile's epilogue.  Tiles are ordered so that each XCD (one
 // L2) works on a contiguous range, in groups of four M-tiles.
+#include <type_traits>
+
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -41,6 +43,7 @@ constexpr int kBK = 128;          // K bytes per stage = one LDS row
 constexpr int kOperand = kTile * kBK;          // 32 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
 constexpr int kGroupM = 4;
+constexpr int kCStage = dev::epilogue_lds_bytes(64);   // epilogue staging per wave
 
 // XOR swizzle of the eight 16-byte chunks of an LDS row: row R keeps logical
 // chunk c at physical chunk c ^ swz(R).  The 16 rows read by one quarter-wave
@@ -67,6 +70,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
   __shared__ __attribute__((aligned(16))) uint32_t sc0[2 * kTile];
   __shared__ __attribute__((aligned(16))) uint32_t sc1[2 * kTile];
+  // per wave: the bias of its 128 columns (the first 256 B of one 1 KiB DMA), and
+  // its output rows on their way to global memory
+  __shared__ __attribute__((aligned(16))) uint8_t bias_lds[4 * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds[4 * kCStage];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
   const int n_tiles = tiles_m * tiles_n;
@@ -83,10 +90,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     n0 = ((wg % per_group) / gsize) * kTile;
   };
 
-  const int t = threadIdx.x, lane = t & 63;
+  const int t = threadIdx.x;
+  int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform (an SGPR)
   const int wn = wave & 1, wm = wave >> 1;
-  const int r = lane & 31, g = lane >> 5;
+  int r = lane & 31, g = lane >> 5;
   const int KB = K / 32;            // scale bytes per row
 
   // Buffer resources with 32-bit offsets (operands are < 2 GiB, checked by the host).
@@ -94,6 +102,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * K, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KB, 0x00020000);
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc((void*)as_, (short)0, M * KB, 0x00020000);
+  const auto rb = __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, EPI >= 1 ? N * 2 : 0, 0x00020000);
 
   // Global -> LDS without registers: each buffer_load ... lds moves 1 KiB per wave
   // (lane i -> LDS bytes [16i, 16i+16) after M0) = 8 rows of 128 B.  Wave w fills
@@ -102,10 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // have swz = ((i/8) >> 1) + 4 (j & 1), hence two lane offsets.  The stage's scale
   // dwords (4 MX blocks of every row) follow with one 4-byte-per-lane load per
   // operand: lane i of wave w -> row 64w + i.
-  const int lrow = lane >> 3, lchunk = lane & 7;
-  const int cx = lchunk ^ (lrow >> 1);
-  const int voff0 = lrow * K + cx * 16, voff1 = lrow * K + (cx ^ 4) * 16;
-  const int vsc = lane * KB;
+  int voff0, voff1, vsc;
   // Every load stays inside its operand.  A wave's 64 rows lie wholly inside or
   // wholly past M (N), both being multiples of 128; rows past the end, and the
   // stages after the workgroup's last tile (valid == false), read rows [0, 64)
@@ -127,8 +133,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc, off_sa, 0, 0);
   };
 
-  const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
-  const int wrow = wn * 128 + r, arow = wm * 128 + r;
+  int x, wrow, arow;
+  // The lane-derived offsets are recomputed at the top of every tile from the lane
+  // id (mbcnt, in a volatile asm block so that it is not hoisted): otherwise they
+  // stay live across the epilogue, get spilled there, and their reloads queue
+  // behind its stores.
+  auto lane_setup = [&](bool opaque) {
+    if (opaque) asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    r = lane & 31;
+    g = lane >> 5;
+    const int lrow = lane >> 3, lchunk = lane & 7;
+    const int cx = lchunk ^ (lrow >> 1);
+    voff0 = lrow * K + cx * 16;
+    voff1 = lrow * K + (cx ^ 4) * 16;
+    vsc = lane * KB;
+    x = swz(r);
+    wrow = wn * 128 + r;
+    arow = wm * 128 + r;
+  };
+  lane_setup(false);
   v8i f0w[4], f0a[4], f1w[4], f1a[4];   // fragments of the first / second 64-K half
   uint32_t scw[4], sca[4], nscw[4], nsca[4];
   // scale dwords of this lane's rows (shifted later so byte 0 / byte 2 hold its block)
@@ -140,49 +163,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     }
   };
 
-  // epi(acc) -> bf16 for the tile at (m0, n0), four consecutive n per 8-byte store.
   auto epilogue = [&](const v16f (&acc)[4][4], int m0, int n0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + 32 * j + r;
-      uint16_t* crow = c + (size_t)m * N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // M, N are multiples of 128: whole 32-row / 32-column MFMA tiles are in or out
-        if (m0 + wm * 128 + 32 * j < M && n0 + wn * 128 + 32 * i < N) {
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
-            float y[4] = {acc[i][j][4 * qd], acc[i][j][4 * qd + 1], acc[i][j][4 * qd + 2], acc[i][j][4 * qd + 3]};
-            if (EPI >= 1) {
-              uint2 b = *(const uint2*)(bias + n);
-              y[0] += dev::bf16_lo(b.x);
-              y[1] += dev::bf16_hi(b.x);
-              y[2] += dev::bf16_lo(b.y);
-              y[3] += dev::bf16_hi(b.y);
-            }
-            if (EPI == 2) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
-            }
-            uint2 o;
-            o.x = dev::pack_bf16x2(y[0], y[1]);
-            o.y = dev::pack_bf16x2(y[2], y[3]);
-            *(uint2*)(crow + n) = o;
-          }
-        }
-      }
-    }
+    // M and N are multiples of 128: a wave's 128 x 128 block is wholly in or out
+    if (m0 + wm * 128 >= M || n0 + wn * 128 >= N) return;
+    dev::epilogue_block<EPI, 64, false>(acc, 1.0f, bias_lds + wave * 1024, c_lds + wave * kCStage, c, N,
+                                        m0 + wm * 128, n0 + wn * 128, lane);
   };
 
   // One stage (buffer cur holds it; nxt holds the next one, possibly of the next tile):
   //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of this stage
   //   B: wait for the next stage's DMA and this wave's reads, barrier (cur is now
-  //      free in every wave, the next stage visible in nxt)
+  //      free in every wave, the next stage visible in nxt); a tile's first stage
+  //      finds the next stage's DMA retired before the previous tile's epilogue and
+  //      waits for its reads only, leaving the epilogue's stores in flight
   //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of the next stage;
   //      DMA of the stage after next (given by dm0, dn0, dk0, dvalid) into cur.
-  auto stage = [&](v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int dm0,
-                   int dn0, int dk0, bool dvalid) {
+  auto stage = [&](auto first_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
+                   int dm0, int dn0, int dk0, bool dvalid) {
     // ---- A
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -202,8 +199,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- B
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
+    if constexpr (decltype(first_)::value) __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);
+    else __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    dev::lds_barrier();
     // ---- C
     read_scales(snxt);
 #pragma unroll
@@ -242,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     dma_stage(lds0, sc0, m0, n0, 0, true);
     dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
+  dev::lds_barrier();
   read_scales(sc0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -258,10 +256,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // single tile.  The K loop is unrolled by two so that every LDS pointer is a fixed
   // object, and the DMA target of stage kt + 2 is chosen with scalar selects (no
   // branch inside the loop body).
+  using First = std::integral_constant<bool, true>;
+  using Later = std::integral_constant<bool, false>;
   for (int ti = 0; ti < my_tiles; ++ti) {
-    // Once per tile: lets the compiler's wait-count tracking retire register spill
-    // stores made outside the K loop, which it would otherwise wait for inside it.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    lane_setup(true);
     const bool has_next = ti + 1 < my_tiles;
     v16f acc[4][4];
 #pragma unroll
@@ -270,23 +268,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    auto one = [&](uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
+    auto one = [&](auto first_, uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
       const int kk = kt + 2;
       const bool nx = kk >= nk;
-      stage(acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next);
+      stage(first_, acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK,
+            !nx || has_next);
     };
-    int kt = 0;
+    one(First(), lds0, lds1, sc0, sc1, 0);
+    // the tile's bias, read by this wave's epilogue from LDS, so that no global load
+    // there queues behind the epilogue's own stores (issued after the first stage:
+    // its reads then need not wait for it)
+    if constexpr (EPI >= 1) dev::load_bias(rb, bias_lds + wave * 1024, n0 + wn * 128, lane);
+    int kt = 1;
     for (; kt + 1 < nk; kt += 2) {
-      one(lds0, lds1, sc0, sc1, kt);
-      one(lds1, lds0, sc1, sc0, kt + 1);
+      one(Later(), lds1, lds0, sc1, sc0, kt);
+      one(Later(), lds0, lds1, sc0, sc1, kt + 1);
     }
-    if (kt < nk) one(lds0, lds1, sc0, sc1, kt);
+    if (kt < nk) one(Later(), lds1, lds0, sc1, sc0, kt);
+    // Retire the next tile's first two stages of DMA now: the stores below share
+    // the counter, and the next tile's first stage then waits for none of them.
+    __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
     epilogue(acc, m0, n0);
     m0 = m0n;
     n0 = n0n;
     if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);   // no DMA outlives the workgroup
 }
 
 template <int AK, int WK>

@@ -49,6 +49,7 @@ constexpr int kRowB = kBK / 2;                 // 64 code bytes per row and stag
 constexpr int kOperand = kTile * kRowB;        // 16 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
 constexpr int kGroupM = 4;
+constexpr int kCStage = dev::epilogue_lds_bytes(128);
 
 // Swizzle of the four 16-byte chunks of a 64-byte LDS row: the 16 rows read by a
 // quarter-wave land on 16 distinct 16-byte bank groups.
@@ -94,6 +95,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
   __shared__ __attribute__((aligned(16))) uint32_t sc0[4 * kTile];
   __shared__ __attribute__((aligned(16))) uint32_t sc1[4 * kTile];
+  // per wave: the bias of its 128 columns (the first 256 B of one 1 KiB DMA)
+  __shared__ __attribute__((aligned(16))) uint8_t bias_lds[4 * 1024];
+  // per wave: output rows on their way to global memory
+  __shared__ __attribute__((aligned(16))) uint8_t c_lds[4 * kCStage];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
   const int n_tiles = tiles_m * tiles_n;
@@ -109,10 +114,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     n0 = ((wg_id % per_group) / gsize) * kTile;
   };
 
-  const int t = threadIdx.x, lane = t & 63;
+  const int t = threadIdx.x;
+  int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave & 1, wm = wave >> 1;
-  const int r = lane & 31, g = lane >> 5;
+  int r = lane & 31, g = lane >> 5;
   const int KP = K / 2, KS = K / 16;    // bytes per row: codes, scales
 
   // 32-bit offsets: operands are < 2 GiB (checked by the host)
@@ -120,13 +126,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * KP, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KS, 0x00020000);
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc((void*)as_, (short)0, M * KS, 0x00020000);
+  const auto rb = __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, EPI >= 1 ? N * 2 : 0, 0x00020000);
 
   // Global -> LDS: one buffer_load ... lds moves 1 KiB per wave = 16 rows of 64 B
   // (lane i -> row i / 4, physical chunk i % 4, i.e. global chunk (i % 4) ^ swz).
   // Rows 16j + i/4 have swz = (i >> 4) & 3 whatever j, so one lane offset serves
   // all four loads of a wave's 64 rows.  Scale dwords: lane i -> row 64w + i.
-  const int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  const int vsc = lane * KS;
+  int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  int vsc = lane * KS;
   // Every load stays inside its operand: a wave's 64 rows lie wholly inside or past
   // M (N); rows past the end, and stages after the last tile, read rows [0, 64).
   // Part p (0..3) of a stage's DMA: code rows 16p..16p+15 of this wave's 64 for W
@@ -156,30 +163,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     for (int p = 0; p < 4; ++p) dma_part(p, buf, sc, m0, n0, k0, valid);
   };
 
-  const int x = swz(r);             // rows wn*128 + 32i + r all share swz(r)
-  const int wrow = wn * 128 + r, arow = wm * 128 + r;
+  int x = swz(r);                   // rows wn*128 + 32i + r all share swz(r)
+  int wrow = wn * 128 + r, arow = wm * 128 + r;
+  // The lane-derived offsets are recomputed at the top of every tile from the lane
+  // id (mbcnt, in a volatile asm block so that it is not hoisted): otherwise they
+  // stay live across the epilogue, get spilled there, and their reloads queue
+  // behind its stores.
+  auto lane_setup = [&]() {
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    r = lane & 31;
+    g = lane >> 5;
+    voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+    vsc = lane * KS;
+    x = swz(r);
+    wrow = wn * 128 + r;
+    arow = wm * 128 + r;
+  };
   uint4 c0w[4], c0a[4], c1w[4], c1a[4];     // codes of the stage's 64-K groups 0 and 1
   v2h s0w[4], s0a[4], s1w[4], s1a[4];       // their scales: {steps 0-1, steps 2-3}
   v8h dw[2][4], da[2][4];                   // dequantized operands, double-buffered by K-step
-  uint32_t rs1w[4], rs1a[4];                // raw group-1 scale dwords of the next stage
 
-  // Scale dwords of a stage: group 0's are converted at once (the previous group 0
-  // is finished by then), group 1's kept raw until the current group 1 is done.
-  // Lane group g uses blocks 2g, 2g + 1 of each group: the g-th 16-bit half.
-  auto read_scales = [&](const uint32_t* sc) {
+  // Scale dwords of group G of a stage, converted to fp16 pairs.  Group 0's are
+  // read while the previous stage's group 1 runs, group 1's while the stage's own
+  // group 0 runs: each when its registers are free.  Lane group g uses blocks
+  // 2g, 2g + 1 of each group: the g-th 16-bit half.
+  auto read_scales = [&](v2h (&sw)[4], v2h (&sa)[4], const uint32_t* sc, int G) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s0w[i] = scale_pair(sc[wrow + 32 * i] >> (16 * g));
-      rs1w[i] = sc[kTile + wrow + 32 * i];
-      s0a[i] = scale_pair(sc[2 * kTile + arow + 32 * i] >> (16 * g));
-      rs1a[i] = sc[3 * kTile + arow + 32 * i];
-    }
-  };
-  auto convert_scales = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s1w[i] = scale_pair(rs1w[i] >> (16 * g));
-      s1a[i] = scale_pair(rs1a[i] >> (16 * g));
+      sw[i] = scale_pair(sc[G * kTile + wrow + 32 * i] >> (16 * g));
+      sa[i] = scale_pair(sc[(2 + G) * kTile + arow + 32 * i] >> (16 * g));
     }
   };
   auto read_codes = [&](uint4 (&cw)[4], uint4 (&ca)[4], const uint8_t* buf, int G) {
@@ -227,55 +239,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
 
   const float alpha = (*ag) * (*wg);
   auto epilogue = [&](const v16f (&acc)[4][4], int m0, int n0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 128 + 32 * j + r;
-      uint16_t* crow = c + (size_t)m * N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // M, N are multiples of 128: whole 32-row / 32-column MFMA tiles are in or out
-        if (m0 + wm * 128 + 32 * j < M && n0 + wn * 128 + 32 * i < N) {
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const int n = n0 + wn * 128 + 32 * i + 8 * qd + 4 * g;
-            float y[4] = {alpha * acc[i][j][4 * qd], alpha * acc[i][j][4 * qd + 1], alpha * acc[i][j][4 * qd + 2],
-                          alpha * acc[i][j][4 * qd + 3]};
-            if (EPI >= 1) {
-              uint2 b = *(const uint2*)(bias + n);
-              y[0] += dev::bf16_lo(b.x);
-              y[1] += dev::bf16_hi(b.x);
-              y[2] += dev::bf16_lo(b.y);
-              y[3] += dev::bf16_hi(b.y);
-            }
-            if (EPI == 2) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] = dev::gelu_tanh(y[e]);
-            }
-            uint2 o;
-            o.x = dev::pack_bf16x2(y[0], y[1]);
-            o.y = dev::pack_bf16x2(y[2], y[3]);
-            *(uint2*)(crow + n) = o;
-          }
-        }
-      }
-    }
+    // M and N are multiples of 128: a wave's 128 x 128 block is wholly in or out
+    if (m0 + wm * 128 >= M || n0 + wn * 128 >= N) return;
+    dev::epilogue_block<EPI, 128, true>(acc, alpha, bias_lds + wave * 1024, c_lds + wave * kCStage, c, N,
+                                        m0 + wm * 128, n0 + wn * 128, lane);
   };
 
   // One stage (cur holds it, nxt the next one):
   //   A: group 0's four K-steps on MFMA || LDS reads of group 1's codes; the last
   //      step dequantizes group 1's first step
-  //   B: wait for the next stage's DMA and this wave's reads, barrier
+  //   B: wait for the next stage's DMA and this wave's reads, barrier (a tile's
+  //      first stage finds the next stage's DMA retired before the previous tile's
+  //      epilogue and waits for its reads only, leaving the epilogue's stores in
+  //      flight)
   //   C: group 1's K-steps || LDS reads of the next stage's scales and group-0 codes,
   //      DMA of the stage after next into cur; the last step dequantizes the next
   //      stage's first step.
   // On entry dw/da[0] hold group 0's first step, dequantized.
-  auto stage = [&](v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt, int dm0,
-                   int dn0, int dk0, bool dvalid) {
+  auto stage = [&](auto first_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
+                   int dm0, int dn0, int dk0, bool dvalid) {
     // ---- A
     read_codes(c1w, c1a, cur, 1);
+    read_scales(s1w, s1a, scur, 1);
     mfma_step(acc, I0());
     dequant(I1(), I1(), c0w, c0a, s0w, s0a);
-    interleave(8, false);
+    interleave(16, false);
     mfma_step(acc, I1());
     dequant(I0(), I2(), c0w, c0a, s0w, s0a);
     interleave(0, false);
@@ -286,10 +274,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     dequant(I0(), I0(), c1w, c1a, s1w, s1a);
     interleave(0, false);
     // ---- B
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    __syncthreads();
+    if constexpr (decltype(first_)::value) __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);
+    else __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    dev::lds_barrier();
     // ---- C
-    read_scales(snxt);
+    read_scales(s0w, s0a, snxt, 0);
     read_codes(c0w, c0a, nxt, 0);
     dma_part(0, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I0());
@@ -305,7 +294,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     interleave(0, true);
     dma_part(3, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I1());
-    convert_scales();
     dequant(I0(), I0(), c0w, c0a, s0w, s0a);
     interleave(0, true);
   };
@@ -320,19 +308,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     dma_stage(lds0, sc0, m0, n0, 0, true);
     dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  __syncthreads();
-  read_scales(sc0);
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
+  dev::lds_barrier();
+  read_scales(s0w, s0a, sc0, 0);
   read_codes(c0w, c0a, lds0, 0);
-  convert_scales();
   dequant(I0(), I0(), c0w, c0a, s0w, s0a);
 
   // Global stage s uses buffer s & 1; with an even number of stages per tile every
   // tile starts in buffer 0 (the launcher gives each workgroup one tile otherwise).
+  using First = std::integral_constant<bool, true>;
+  using Later = std::integral_constant<bool, false>;
   for (int ti = 0; ti < my_tiles; ++ti) {
-    // Once per tile: lets the compiler's wait-count tracking retire register spill
-    // stores made outside the K loop, which it would otherwise wait for inside it.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    lane_setup();
     const bool has_next = ti + 1 < my_tiles;
     v16f acc[4][4];
 #pragma unroll
@@ -341,23 +328,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    auto one = [&](uint8_t* b0, uint8_t* b1, uint32_t* t0, uint32_t* t1, int kt) {
+    auto one = [&](auto first_, uint8_t* b0, uint8_t* b1, uint32_t* t0, uint32_t* t1, int kt) {
       const int kk = kt + 2;
       const bool nx = kk >= nk;
-      stage(acc, b0, b1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next);
+      stage(first_, acc, b0, b1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK,
+            !nx || has_next);
     };
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      one(lds0, lds1, sc0, sc1, kt);
-      one(lds1, lds0, sc1, sc0, kt + 1);
+    one(First(), lds0, lds1, sc0, sc1, 0);
+    if constexpr (EPI >= 1) {
+      // the tile's bias, read by this wave's epilogue from LDS, so that no global
+      // load there queues behind the epilogue's own stores; any later vmcnt(0)
+      // retires it, and this wave's previous epilogue has finished with the slot
+      dev::load_bias(rb, bias_lds + wave * 1024, n0 + wn * 128, lane);
     }
-    if (kt < nk) one(lds0, lds1, sc0, sc1, kt);
+    int kt = 1;
+    for (; kt + 1 < nk; kt += 2) {
+      one(Later(), lds1, lds0, sc1, sc0, kt);
+      one(Later(), lds0, lds1, sc0, sc1, kt + 1);
+    }
+    if (kt < nk) one(Later(), lds1, lds0, sc1, sc0, kt);
+    // Retire the next tile's first two stages of DMA now: the stores below share
+    // the counter, and the next tile's first stage then waits for none of them.
+    __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
     epilogue(acc, m0, n0);
     m0 = m0n;
     n0 = n0n;
     if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);   // no DMA outlives the workgroup
 }
 
 }  // namespace
