@@ -76,6 +76,89 @@ def measured_traffic(kernel):
     return rec
 
 
+KERNEL_SOURCES = {  # HIP kernel -> sources whose text decides its code
+    "k_quant_mxfp8": ["quant_mxfp8.hip"],
+    "k_amax_partials": ["quant_nvfp4.hip"],
+    "k_quant_nvfp4": ["quant_nvfp4.hip"],
+    "k_gemm_mxfp8": ["gemm_mxfp8.hip"],
+    "k_gemm_nvfp4": ["gemm_nvfp4.hip"],
+}
+
+
+def step_dispatches():
+    """(op name, kernel function) of every dispatch of one step, in launch order."""
+    out = []
+    for name, _, _, epi in MX_LINEARS:
+        out.append(("quant_mxfp8_" + name, "k_quant_mxfp8<0>"))
+        out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
+    for name, _, _, epi in NV_LINEARS:
+        out.append(("quant_nvfp4_" + name, "k_amax_partials"))
+        out.append(("quant_nvfp4_" + name, "k_quant_nvfp4"))
+        out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
+    return out
+
+
+def record_traffic(fetch_db, write_db):
+    """profiles/hbm_traffic.json from the two counter runs
+        rocprofv3 --pmc FETCH_SIZE --kernel-trace ... -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration
+        rocprofv3 --pmc WRITE_SIZE --kernel-trace ... (same)
+    The step's dispatches are the ones right after the 1 GiB calibration copy; each
+    counter is scaled by what it reads for that copy (1 GiB read, 1 GiB written)."""
+    import sqlite3
+
+    def per_dispatch(db):
+        cur = sqlite3.connect(db).cursor()
+        rows = cur.execute("select k.dispatch_id, k.name, sum(p.counter_value) from pmc_events p join kernels k "
+                           "on k.dispatch_id = p.dispatch_id group by k.dispatch_id order by k.dispatch_id")
+        out = []
+        for did, name, kib in rows:
+            short = name.replace("mxq::(anonymous namespace)::", "").replace("void ", "").split("(")[0].strip()
+            out.append((did, short, float(kib)))
+        return out
+
+    fetch, write = per_dispatch(fetch_db), per_dispatch(write_db)
+    scale, step = {}, {}
+    for counter, rows in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        copies = [i for i, (_, n, _) in enumerate(rows) if "copyBuffer" in n]
+        if not copies:
+            raise SystemExit("no calibration copy in %s" % counter)
+        i = max(copies, key=lambda j: rows[j][2])
+        scale[counter] = round((1 << 20) / rows[i][2], 3)       # KiB of a 1 GiB transfer / counted KiB
+        expect = step_dispatches()
+        got = rows[i + 1:i + 1 + len(expect)]
+        if [n for _, n, _ in got] != [k for _, k in expect]:
+            raise SystemExit("%s: dispatches after the copy are %s" % (counter, [n for _, n, _ in got]))
+        step[counter] = [kib for _, _, kib in got]
+    rec = {}
+    for idx, (op, kernel) in enumerate(step_dispatches()):
+        base = kernel.split("<")[0]
+        r = rec.setdefault(kernel, {
+            "sources": ["microscaling_quantized_dit_amd/csrc/" + f for f in KERNEL_SOURCES[base]] +
+                       ["microscaling_quantized_dit_amd/csrc/mxq_internal.h"],
+            "launches": {}, "scale": scale, "summary": "profiles/flux_dit_step_hbm_counters.md"})
+        r["launches"][op] = {"FETCH_SIZE_KiB": step["FETCH_SIZE"][idx], "WRITE_SIZE_KiB": step["WRITE_SIZE"][idx]}
+    for kernel, r in rec.items():
+        n = len(r["launches"])
+        rd = sum(v["FETCH_SIZE_KiB"] for v in r["launches"].values()) * 1024 * scale["FETCH_SIZE"] / n
+        wr = sum(v["WRITE_SIZE_KiB"] for v in r["launches"].values()) * 1024 * scale["WRITE_SIZE"] / n
+        r["read_bytes_per_launch"], r["write_bytes_per_launch"] = int(rd), int(wr)
+        r["bytes_per_launch"] = int(rd) + int(wr)
+        h = hashlib.sha256()
+        for src in r["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        r["sha256"] = h.hexdigest()
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print("scale: FETCH_SIZE x%.3f, WRITE_SIZE x%.3f" % (scale["FETCH_SIZE"], scale["WRITE_SIZE"]))
+    print("| Dispatch | FETCH KiB | WRITE KiB | HBM read | HBM write |")
+    print("|---|---:|---:|---:|---:|")
+    for idx, (op, kernel) in enumerate(step_dispatches()):
+        fk, wk = step["FETCH_SIZE"][idx], step["WRITE_SIZE"][idx]
+        print("| `%s` %s | %.0f | %.0f | %.1f MB | %.1f MB |" % (kernel, op, fk, wk, fk * 1024 * scale["FETCH_SIZE"] / 1e6,
+                                                              wk * 1024 * scale["WRITE_SIZE"] / 1e6))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -85,6 +168,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     p.add_argument("--cpu-rows", type=int, default=1536, help="rows per linear in the CPU-baseline sample")
+    p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                   help="write profiles/hbm_traffic.json from two rocprofv3 counter databases (no GPU needed)")
     return p.parse_args()
 
 
@@ -286,6 +371,9 @@ def cpu_baseline(rows_per_linear: int):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the hot path runs on a single MI355X); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
