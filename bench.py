@@ -197,9 +197,11 @@ class Workload:
             as_ = torch.empty((M_NV, K // 16), dtype=torch.uint8, device=dev)
             ag = torch.empty((1,), dtype=torch.float32, device=dev)
             ws_buf = torch.empty((max(mxq.nvfp4_workspace_size(M_NV, K), 4),), dtype=torch.uint8, device=dev)
+            g_ws = mxq.gemm_nvfp4_workspace_size(M_NV, N, K)
+            g_buf = torch.empty((g_ws,), dtype=torch.uint8, device=dev) if g_ws else None
             c = torch.empty((M_NV, N), dtype=torch.bfloat16, device=dev)
             self.nv.append(dict(name=name, N=N, K=K, epi=epi, x=x, wq=wq, ws=ws, wg=wg, aq=aq, as_=as_, ag=ag,
-                                wsb=ws_buf, c=c))
+                                wsb=ws_buf, gws=g_buf, c=c))
             del w
         torch.cuda.synchronize()
 
@@ -229,7 +231,7 @@ class Workload:
                         lambda L=L: mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], L["ag"]), workspace=L["wsb"])))
             out.append(("gemm_nvfp4_" + L["name"], "gemm_nv",
                         lambda L=L: mxq.gemm_nvfp4(L["aq"], L["as_"], L["ag"], L["wq"], L["ws"], L["wg"],
-                                                   out=L["c"])))
+                                                   out=L["c"], workspace=L["gws"])))
         return out
 
     def work(self):

@@ -194,17 +194,32 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
                           void* c, void* stream);
 
 /*
+ * Bytes of device workspace mxq_gemm_nvfp4 can use for this shape on the current
+ * device; 0 when it has no use for one (or the shape is invalid).  With it, the
+ * output tiles that would otherwise run in a partial last round on the compute
+ * units are cut along K into ranges computed side by side, and their fp32 partial
+ * sums are added by a second kernel before the epilogue.
+ */
+size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
  * NVFP4 block-scaled GEMM [P1 NVFP4 paragraph; P2 §3.1].
  *   C[m, n] = epi( s_ga s_gw sum_k val(a_q) val(a_s[m,k/16]) val(w_q) val(w_s[n,k/16])
  *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.
  *   a_q, a_scales, a_global : packed E2M1 [M, K/2], E4M3 [M, K/16], device fp32 s_ga.
  *   w_q, w_scales, w_global : packed E2M1 [N, K/2], E4M3 [N, K/16], device fp32 s_gw.
  *   M, N, K, bias, epi, c   : as mxq_gemm_mxfp8.
+ *   workspace, ws_bytes     : NULL (no split), or device scratch of at least
+ *                             mxq_gemm_nvfp4_workspace_size(M, N, K) bytes, 16-byte
+ *                             aligned (else MXQ_ERROR_WORKSPACE / MXQ_ERROR_MISALIGNED);
+ *                             calls sharing one must be ordered on one stream.
+ *   The fp32 additions of a split tile's parts come in a different order than an
+ *   unsplit accumulation; results agree within the GEMM tolerance, not bit for bit.
  */
 mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_global,
                           const void* w_q, const void* w_scales, const float* w_global,
                           int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi,
-                          void* c, void* stream);
+                          void* c, void* workspace, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* mxq_status_string(mxq_status s);

@@ -34,7 +34,8 @@ _lock = threading.Lock()
 _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
-           "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4",
+           "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size",
+           "mxq_gemm_nvfp4",
            "mxq_gemm_bf16_fp8w", "mxq_status_string", "mxq_last_error"]
 
 
@@ -69,7 +70,9 @@ def load():
         lib.mxq_quantize_fp8_weight.argtypes = [P, i64, i64, P, P, P, P, sz, P]
         lib.mxq_gemm_bf16_fp8w.argtypes = [P, P, P, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, P, P]
-        lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P]
+        lib.mxq_gemm_nvfp4_workspace_size.argtypes = [i64, i64, i64]
+        lib.mxq_gemm_nvfp4_workspace_size.restype = sz
+        lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P, sz, P]
         lib.mxq_status_string.argtypes = [i32]
         lib.mxq_status_string.restype = ctypes.c_char_p
         lib.mxq_last_error.argtypes = []
@@ -246,8 +249,16 @@ def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e
     return c
 
 
-def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, stream=None):
-    """C[M, N] = epi(s_ga s_gw A . W^T) in bf16 from NVFP4 operands."""
+def gemm_nvfp4_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace gemm_nvfp4 can use for this shape on the current device."""
+    return int(load().mxq_gemm_nvfp4_workspace_size(M, N, K))
+
+
+def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, workspace=None, split=True,
+               stream=None):
+    """C[M, N] = epi(s_ga s_gw A . W^T) in bf16 from NVFP4 operands.  With split
+    (default), a workspace (given, or allocated here) lets the tiles of a partial
+    last round be split along K."""
     torch = _torch()
     for t, n in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, n)
@@ -265,8 +276,17 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, stre
         _need(bias, torch.bfloat16, "bias")
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
     lib = load()
+    ws, nbytes = None, 0
+    if split:
+        need = int(lib.mxq_gemm_nvfp4_workspace_size(M, N, K))
+        if workspace is not None:
+            _need(workspace, torch.uint8, "workspace")
+            ws, nbytes = workspace, workspace.numel()
+        elif need:
+            ws = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
+            nbytes = need
     _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
-                              M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
+                              M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes, _stream(stream)))
     return c
 
 

@@ -48,7 +48,6 @@ constexpr int kBK = 128;                       // K values per stage
 constexpr int kRowB = kBK / 2;                 // 64 code bytes per row and stage
 constexpr int kOperand = kTile * kRowB;        // 16 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
-constexpr int kGroupM = 4;
 constexpr int kCStage = dev::epilogue_lds_bytes(128);
 
 // Swizzle of the four 16-byte chunks of a 64-byte LDS row: the 16 rows read by a
@@ -85,11 +84,14 @@ __device__ __forceinline__ uint32_t word(const uint4& v) {
   return J == 0 ? v.x : J == 1 ? v.y : J == 2 ? v.z : v.w;
 }
 
-template <int EPI>
+// PART = false: tiles [0, sp.dp_tiles) whole, round-robin over the workgroups.
+// PART = true: one K range of a split tile per workgroup, its fp32 sum into
+// sp.partial (the fixup kernel completes the tile).
+template <int EPI, bool PART>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const float* __restrict__ ag,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const float* __restrict__ wg,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N, int K) {
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N, int K, GemmSplit sp) {
   // two stage buffers (codes; scale dwords [W d0, W d1, A d0, A d1][row]) as distinct objects
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
@@ -101,17 +103,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   __shared__ __attribute__((aligned(16))) uint8_t c_lds[4 * kCStage];
 
   const int tiles_m = (M + kTile - 1) / kTile, tiles_n = (N + kTile - 1) / kTile;
-  const int n_tiles = tiles_m * tiles_n;
   const int nk = K / kBK;
-  const int my_tiles = (n_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  auto origin = [&](int ti, int& m0, int& n0) {
-    const int v = blockIdx.x + ti * gridDim.x;
-    const int wg_id = dev::xcd_remap(v, n_tiles);
-    const int per_group = kGroupM * tiles_n;
-    const int first_m = (wg_id / per_group) * kGroupM;
-    const int gsize = min(tiles_m - first_m, kGroupM);
-    m0 = (first_m + (wg_id % per_group) % gsize) * kTile;
-    n0 = ((wg_id % per_group) / gsize) * kTile;
+  // This workgroup's tiles: whole tiles blockIdx + i * gridDim below dp_tiles, or
+  // (PART) one K range of a split tile.  Every tile has an even number >= 2 of
+  // stages when the launch is persistent.
+  const int my_tiles = PART ? 1 : (sp.dp_tiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  struct Tile {
+    int m0, n0, kb, nkt;   // origin, first K stage, stages
+  };
+  auto tile_info = [&](int ti, Tile& T) {
+    int v;
+    if constexpr (PART) {
+      v = sp.dp_tiles + (int)blockIdx.x / sp.parts;
+      T.nkt = nk / sp.parts;
+      T.kb = ((int)blockIdx.x % sp.parts) * T.nkt;
+    } else {
+      v = blockIdx.x + ti * gridDim.x;
+      T.kb = 0;
+      T.nkt = nk;
+    }
+    dev::tile_origin(v, tiles_m, tiles_n, T.m0, T.n0);
   };
 
   const int t = threadIdx.x;
@@ -298,15 +309,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     interleave(0, true);
   };
 
-  int m0 = 0, n0 = 0, m0n = 0, n0n = 0;
-  origin(0, m0, n0);
-  if (my_tiles > 1) origin(1, m0n, n0n);
+  Tile cu{0, 0, 0, 2}, nx{0, 0, 0, 2};
+  tile_info(0, cu);
+  if (my_tiles > 1) tile_info(1, nx);
 
   // Prologue: the first two stages in flight; wait; stage 0's scales, codes and first step.
   {
-    const bool nx1 = nk < 2;
-    dma_stage(lds0, sc0, m0, n0, 0, true);
-    dma_stage(lds1, sc1, nx1 ? m0n : m0, nx1 ? n0n : n0, nx1 ? 0 : kBK, !nx1 || my_tiles > 1);
+    const bool nx1 = cu.nkt < 2;
+    dma_stage(lds0, sc0, cu.m0, cu.n0, cu.kb * kBK, true);
+    dma_stage(lds1, sc1, nx1 ? nx.m0 : cu.m0, nx1 ? nx.n0 : cu.n0, (nx1 ? nx.kb : cu.kb + 1) * kBK,
+              !nx1 || my_tiles > 1);
   }
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
   dev::lds_barrier();
@@ -315,7 +327,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   dequant(I0(), I0(), c0w, c0a, s0w, s0a);
 
   // Global stage s uses buffer s & 1; with an even number of stages per tile every
-  // tile starts in buffer 0 (the launcher gives each workgroup one tile otherwise).
+  // tile starts in buffer 0 (the launcher gives each workgroup one tile otherwise,
+  // and cuts split tiles into even ranges).
   using First = std::integral_constant<bool, true>;
   using Later = std::integral_constant<bool, false>;
   for (int ti = 0; ti < my_tiles; ++ti) {
@@ -328,59 +341,91 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // DMA of stage kt + 2: this tile's, or the next tile's first two
     auto one = [&](auto first_, uint8_t* b0, uint8_t* b1, uint32_t* t0, uint32_t* t1, int kt) {
       const int kk = kt + 2;
-      const bool nx = kk >= nk;
-      stage(first_, acc, b0, b1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK,
-            !nx || has_next);
+      const bool in_next = kk >= cu.nkt;
+      stage(first_, acc, b0, b1, t0, t1, in_next ? nx.m0 : cu.m0, in_next ? nx.n0 : cu.n0,
+            (in_next ? nx.kb + kk - cu.nkt : cu.kb + kk) * kBK, !in_next || has_next);
     };
     one(First(), lds0, lds1, sc0, sc1, 0);
     if constexpr (EPI >= 1) {
       // the tile's bias, read by this wave's epilogue from LDS, so that no global
       // load there queues behind the epilogue's own stores; any later vmcnt(0)
       // retires it, and this wave's previous epilogue has finished with the slot
-      dev::load_bias(rb, bias_lds + wave * 1024, n0 + wn * 128, lane);
+      if constexpr (!PART) dev::load_bias(rb, bias_lds + wave * 1024, cu.n0 + wn * 128, lane);
     }
     int kt = 1;
-    for (; kt + 1 < nk; kt += 2) {
+    for (; kt + 1 < cu.nkt; kt += 2) {
       one(Later(), lds1, lds0, sc1, sc0, kt);
       one(Later(), lds0, lds1, sc0, sc1, kt + 1);
     }
-    if (kt < nk) one(Later(), lds1, lds0, sc1, sc0, kt);
+    if (kt < cu.nkt) one(Later(), lds1, lds0, sc1, sc0, kt);
     // Retire the next tile's first two stages of DMA now: the stores below share
     // the counter, and the next tile's first stage then waits for none of them.
     __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
-    epilogue(acc, m0, n0);
-    m0 = m0n;
-    n0 = n0n;
-    if (ti + 2 < my_tiles) origin(ti + 2, m0n, n0n);
+    if constexpr (PART)
+      dev::store_partial(acc, sp.partial + (size_t)blockIdx.x * kTile * kTile, c_lds + wave * kCStage, wm, wn, lane);
+    else
+      epilogue(acc, cu.m0, cu.n0);
+    cu = nx;
+    if (ti + 2 < my_tiles) tile_info(ti + 2, nx);
   }
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);   // no DMA outlives the workgroup
 }
 
 }  // namespace
 
-// Shapes reaching here are validated: M, N, K positive multiples of 128, epi 0..2.
+static GemmSplit nvfp4_split(int64_t M, int64_t N, int64_t K) {
+  const int tiles = (int)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile));
+  const int nk = (int)(K / kBK);
+  if (nk % 2 != 0) return GemmSplit{tiles, 0, nullptr};   // not persistent
+  return plan_gemm_split(tiles, device_compute_units(), nk);
+}
+
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return gemm_split_bytes(nvfp4_split(M, N, K), (int)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile)));
+}
+
+// Shapes reaching here are validated: M, N, K positive multiples of 128, epi 0..2;
+// workspace is NULL or holds gemm_nvfp4_workspace_bytes(M, N, K).
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q, const void* w_s,
                              const float* w_g, int64_t M, int64_t N, int64_t K, const void* bias, int epi, void* c,
-                             hipStream_t stream) {
+                             void* workspace, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
   // persistent (one workgroup per CU) when a tile has an even number of K stages;
-  // otherwise one workgroup per tile
+  // otherwise one workgroup per tile.  With a workspace, the tiles of a partial
+  // last round are split along K: a second launch computes the K ranges, the
+  // fixup kernel completes them (gemm_fixup.hip).
   const int cus = device_compute_units();
-  const int grid_n = ((k / kBK) % 2 != 0 || tiles < cus) ? tiles : cus;
-  dim3 grid(grid_n), block(kThreads);
+  const bool persistent = (k / kBK) % 2 == 0 && tiles >= cus;
+  GemmSplit sp{tiles, 0, nullptr};
+  if (persistent && workspace) {
+    sp = nvfp4_split(M, N, K);
+    sp.partial = (float*)workspace;
+  }
   auto A = (const uint8_t*)a_q;
   auto As = (const uint8_t*)a_s;
   auto W = (const uint8_t*)w_q;
   auto Ws = (const uint8_t*)w_s;
   auto B = (const uint16_t*)bias;
   auto C = (uint16_t*)c;
-  if (epi == 0) hipLaunchKernelGGL(k_gemm_nvfp4<0>, grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k);
-  else if (epi == 1) hipLaunchKernelGGL(k_gemm_nvfp4<1>, grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k);
-  else hipLaunchKernelGGL(k_gemm_nvfp4<2>, grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k);
-  return hipGetLastError();
+  dim3 block(kThreads);
+  dim3 grid(persistent ? cus : tiles);
+  if (epi == 0)
+    hipLaunchKernelGGL((k_gemm_nvfp4<0, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+  else if (epi == 1)
+    hipLaunchKernelGGL((k_gemm_nvfp4<1, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+  else
+    hipLaunchKernelGGL((k_gemm_nvfp4<2, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !sp.parts) return e;
+  dim3 grid_p((tiles - sp.dp_tiles) * sp.parts);
+  hipLaunchKernelGGL((k_gemm_nvfp4<0, true>), grid_p, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gemm_fixup(sp, M, N, a_g, w_g, bias, epi, c, stream);
 }
 
 }  // namespace mxq

@@ -213,9 +213,16 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
                   "mxq_gemm_mxfp8 launch");
 }
 
+size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M % 128 || N % 128 || K % 128) return 0;
+  if (M >= kMax32 || N >= kMax32 || K >= kMax32) return 0;
+  return mxq::gemm_nvfp4_workspace_bytes(M, N, K);
+}
+
 mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_global, const void* w_q,
                           const void* w_scales, const float* w_global, int64_t M, int64_t N, int64_t K,
-                          const void* bias, mxq_epilogue epi, void* c, void* stream) {
+                          const void* bias, mxq_epilogue epi, void* c, void* workspace, size_t ws_bytes,
+                          void* stream) {
   if (!a_q || !a_scales || !a_global || !w_q || !w_scales || !w_global)
     return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
   mxq_status s = check_gemm_common(M, N, K, bias, epi, c, 1, 2);
@@ -224,10 +231,16 @@ mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_
     return fail(MXQ_ERROR_MISALIGNED, "operands must be 16-byte aligned");
   if (((uintptr_t)a_global & 3u) || ((uintptr_t)w_global & 3u))
     return fail(MXQ_ERROR_MISALIGNED, "global scale pointers must be 4-byte aligned");
+  if (workspace) {
+    if (!aligned16(workspace)) return fail(MXQ_ERROR_MISALIGNED, "workspace must be 16-byte aligned");
+    const size_t need = mxq::gemm_nvfp4_workspace_bytes(M, N, K);
+    if (ws_bytes < need)
+      return fail(MXQ_ERROR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  }
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
   return launched(mxq::launch_gemm_nvfp4(a_q, a_scales, a_global, w_q, w_scales, w_global, M, N, K, bias, (int)epi,
-                                         c, (hipStream_t)stream),
+                                         c, workspace, (hipStream_t)stream),
                   "mxq_gemm_nvfp4 launch");
 }
 

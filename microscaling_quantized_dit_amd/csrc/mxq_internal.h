@@ -27,6 +27,30 @@ hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running
 hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const float* scale_in, void* q,
                                      float* scale_out, uint32_t* partials, hipStream_t stream);
 
+// Work division of a persistent GEMM launch over its 256 x 256 output tiles (ids in
+// the order of dev::tile_origin).  Tiles [0, dp_tiles) are computed whole, the same
+// number by every workgroup.  Each remaining tile is cut along K into `parts`
+// equal ranges; workgroup u < (n_tiles - dp_tiles) * parts computes range u % parts
+// of tile dp_tiles + u / parts into partial[u] (256 x 256 fp32, row-major), and
+// launch_gemm_fixup sums the parts and applies the epilogue.  parts == 0: no split.
+struct GemmSplit {
+  int dp_tiles;
+  int parts;
+  float* partial;
+};
+
+// Split for `tiles` tiles of `nk` K-stages on `cus` persistent workgroups: the
+// remaining tiles cut into the most parts that still fit in one round, each part
+// an even number (>= 2) of stages; parts = 0 when there is no partial last round
+// or no such cut.  Bytes of partial tiles it needs.
+GemmSplit plan_gemm_split(int tiles, int cus, int nk);
+size_t gemm_split_bytes(const GemmSplit& sp, int tiles);
+
+// Sums the K parts of the split tiles and writes epi(alpha * sum) to C (bf16),
+// alpha = (*alpha_a) * (*alpha_b) with a null pointer read as 1.
+hipError_t launch_gemm_fixup(const GemmSplit& sp, int64_t M, int64_t N, const float* alpha_a, const float* alpha_b,
+                             const void* bias, int epi, void* c, hipStream_t stream);
+
 hipError_t launch_gemm_w8(const void* a, const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
                           const void* bias, int epi, void* c, hipStream_t stream);
 
@@ -34,9 +58,11 @@ hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const
                              const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
                              const void* bias, int epi, void* c, hipStream_t stream);
 
+// workspace: NULL (no split) or at least gemm_nvfp4_workspace_bytes(M, N, K) bytes
+size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q,
                              const void* w_s, const float* w_g, int64_t M, int64_t N, int64_t K,
-                             const void* bias, int epi, void* c, hipStream_t stream);
+                             const void* bias, int epi, void* c, void* workspace, hipStream_t stream);
 
 }  // namespace mxq
 
@@ -183,6 +209,53 @@ __device__ __forceinline__ int xcd_remap(int wg, int n_wg) {
   int per = n_wg / n_xcd;
   if (wg >= per * n_xcd) return wg;
   return (wg % n_xcd) * per + wg / n_xcd;
+}
+
+// Origin of output tile v of a GEMM with tiles_m x tiles_n tiles of 256 x 256:
+// ids spread round-robin over the XCDs become contiguous ranges per XCD, and a
+// range walks groups of four M-tiles column by column, so that neighbouring
+// workgroups share A and W panels in their L2.  A bijection on [0, tiles).
+__device__ __forceinline__ void tile_origin(int v, int tiles_m, int tiles_n, int& m0, int& n0) {
+  const int group_m = 4;
+  const int wg = xcd_remap(v, tiles_m * tiles_n);
+  const int per_group = group_m * tiles_n;
+  const int first_m = (wg / per_group) * group_m;
+  const int gsize = min(tiles_m - first_m, group_m);
+  m0 = (first_m + (wg % per_group) % gsize) * 256;
+  n0 = ((wg % per_group) / gsize) * 256;
+}
+
+// fp32 partial tile of a split unit: the wave's 128 x 128 block of acc (layout as
+// for epilogue_block) into partial (256 x 256 fp32, row-major) at its place
+// (wm, wn).  Staged like epilogue_block, 32 rows x 64 columns at a time through
+// the same epilogue_lds_bytes(128) of LDS, so every store covers 256-byte rows.
+__device__ __forceinline__ void store_partial(const v16f_t (&acc)[4][4], float* partial, uint8_t* stage, int wm,
+                                              int wn, int lane) {
+  constexpr int kRow = 4 * 64 + 16;
+  const int r = lane & 31, g = lane >> 5;
+  const int srow = lane >> 4, chunk = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * h + ii;
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int col = 32 * ii + 8 * qd + 4 * g;   // within the 64-column half
+          *(float4*)(stage + r * kRow + 4 * col) =
+              float4{acc[i][j][4 * qd], acc[i][j][4 * qd + 1], acc[i][j][4 * qd + 2], acc[i][j][4 * qd + 3]};
+        }
+      }
+      float* dst = partial + (wm * 128 + 32 * j) * 256 + wn * 128 + 64 * h + 4 * chunk;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = 4 * q + srow;
+        *(float4*)(dst + row * 256) = *(const float4*)(stage + row * kRow + 16 * chunk);
+      }
+    }
+  }
 }
 
 }  // namespace dev

@@ -38,7 +38,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_quantize_nvfp4_workspace_size",
-              "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_status_string", "mxq_last_error"]:
+              "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size", "mxq_gemm_nvfp4", "mxq_status_string",
+              "mxq_last_error"]:
         assert s in syms
 
 
@@ -151,13 +152,22 @@ def test_gemm_mxfp8_validation(lib):
 
 
 def test_gemm_nvfp4_validation(lib):
-    def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE):
-        return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, M, N, K, bias, epi, c, None)
+    def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE, ws=None, nbytes=0):
+        return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, M, N, K, bias, epi, c, ws, nbytes, None)
 
     assert call(ag=None) == INVALID
     assert call(N=100) == SHAPE
     assert call(epi=2) == INVALID
     assert call(ag=FAKE + 1) == MISALIGNED
+    # a shape with a partial last round (17 x 16 tiles on 256 compute units, the
+    # count assumed without a device) wants a workspace; too small a one is refused
+    need = lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1024)
+    assert need == 16 * 4 * 256 * 256 * 4               # 16 leftover tiles, 4 K-parts, fp32
+    assert call(M=4352, N=4096, K=1024, ws=FAKE, nbytes=need - 1) == WORKSPACE
+    assert call(M=4352, N=4096, K=1024, ws=FAKE + 8, nbytes=need) == MISALIGNED
+    assert lib.mxq_gemm_nvfp4_workspace_size(4096, 4096, 1024) == 0    # 256 tiles: one full round
+    assert lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1152) == 0    # odd stage count: no persistence
+    assert lib.mxq_gemm_nvfp4_workspace_size(100, 4096, 1024) == 0
 
 
 @pytest.mark.skipif(gpu_available(), reason="device gate is only observable without a GPU")

@@ -222,6 +222,51 @@ def test_long_sequence(mxq, N):
     _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias", rows=rows), "cfg5 nv")
 
 
+# ------------------------------------------- split tiles of a partial last round
+
+def _tile_origins(M, N):
+    """Origin of every 256 x 256 output tile id in the GEMMs' tile order: ids spread
+    round-robin over the 8 XCDs become contiguous ranges, then groups of four
+    M-tiles are walked column by column."""
+    tm, tn = -(-M // 256), -(-N // 256)
+    n = tm * tn
+    per = n // 8
+    out = []
+    for v in range(n):
+        wg = (v % 8) * per + v // 8 if v < per * 8 else v
+        first_m = (wg // (4 * tn)) * 4
+        gs = min(tm - first_m, 4)
+        out.append(((first_m + (wg % (4 * tn)) % gs) * 256, ((wg % (4 * tn)) // gs) * 256))
+    return out
+
+
+@pytest.mark.parametrize("epi", ["none", "bias_gelu"])
+def test_nvfp4_split_tail(mxq, epi):
+    """One full round of tiles plus a partial one (16 tile columns, one more tile
+    row than the compute units fill): the partial round's tiles are cut along K
+    and completed by the fixup kernel.  The result agrees with the unsplit GEMM
+    over the whole output, and rows inside split tiles with the oracle."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N, K = 4096, 1024
+    M = 256 * (cus // 16 + 1)
+    assert mxq.gemm_nvfp4_workspace_size(M, N, K) > 0
+    a = inputs.flux_activation(M, K, seed=7, stream="split/A")
+    w = inputs.weight(N, K, seed=7, stream="split/W")
+    b = inputs.bias(N, K, seed=7, stream="split/b")
+    A, W = NV(a), NV(w)
+    bias = inputs.to_torch(b, "cuda") if epi != "none" else None
+    g = _bf16_out(mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, bias=bias, epi=epi))
+    g0 = _bf16_out(mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, bias=bias, epi=epi, split=False))
+    _assert_close(g, g0, "split vs unsplit")
+    tiles = _tile_origins(M, N)
+    split = tiles[len(tiles) - len(tiles) % cus:]
+    rows = np.array(sorted({m0 + off for m0, _ in split for off in (0, 97, 255)}))
+    r = oracle.gemm_nvfp4(A.q, A.s, A.g, W.q, W.s, W.g, bias=b if epi != "none" else None, epi=EPIS[epi],
+                          row_idx=rows)
+    _assert_close(g[rows], r, "split rows vs oracle")
+
+
 # ---------------------------------------------- weight-only FP8 (bf16 x E4M3)
 
 def run_w8(mxq, a, w_bits, bias=None, epi="none", rows=None, scale=None):
