@@ -279,6 +279,80 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=EPI_NONE, row_idx=No
     return linear(a, w, alpha, bias, epi)
 
 
+# ------------------------------------------------------------- FP8 attention
+#
+# Reading of "multi-head attention in FP8" (page "NVIDIA Blackwell平台FP4量化技术解析与
+# 图像生成优化", section 2.1, mixed-precision configuration: fully connected layers
+# in FP4, multi-head attention in FP8, normalization in FP16): per head,
+# O = softmax(Q K^T / sqrt(d)) V with
+#   - Q, K, V each quantized per tensor to E4M3 (the per-tensor quantizer above);
+#   - both products on FP8 operands: S from the Q and K codes, and P V with the
+#     probabilities P encoded as E4M3 codes of P * 256 (P <= 1, so at most 256);
+#   - softmax in the online (running-maximum) form over key blocks of 64 in key
+#     order: for each block, m' = max(m, max S), P = exp(S - m'), the running
+#     normalizer l = l * exp(m - m') + sum P (unquantized P) and the running
+#     numerator acc = acc * exp(m - m') + q(P) V;  O = acc / l.
+# The quantized P depends on the running maximum at its block, which is why the
+# oracle takes the blocked algorithm's steps in order.
+
+ATTN_BLOCK = 64          # keys per online-softmax block
+ATTN_P_SCALE = 256.0     # P is encoded as E4M3 codes of P * 256
+
+
+def attention_p_quantize(p: np.ndarray) -> np.ndarray:
+    """q(P) = val(RN_E4M3(P * 256)) / 256 elementwise for 0 <= P <= 1 (fp64)."""
+    p = np.asarray(p, np.float64)
+    codes = round_quotient_array(E4M3, (p * ATTN_P_SCALE).ravel(), 1.0)
+    return (_table("e4m3")[codes] / ATTN_P_SCALE).reshape(p.shape)
+
+
+def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize_p: bool = True) -> np.ndarray:
+    """Online-softmax attention of fp64 rows q [R, d] over k, v [L, d]:
+    acc / l as above, with scores S = sm_scale * q . k.  quantize_p=False keeps P
+    unquantized (plain softmax attention, computed blockwise)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    R, L = q.shape[0], k.shape[0]
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, v.shape[1]))
+    for b0 in range(0, L, block):
+        S = (q @ k[b0:b0 + block].T) * sm_scale
+        m_new = np.maximum(m, S.max(axis=1))
+        alpha = np.exp(m - m_new)
+        P = np.exp(S - m_new[:, None])
+        l = l * alpha + P.sum(axis=1)
+        Pq = attention_p_quantize(P) if quantize_p else P
+        acc = acc * alpha[:, None] + Pq @ v[b0:b0 + block]
+        m = m_new
+    return acc / l[:, None]
+
+
+def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: int, row_idx=None) -> np.ndarray:
+    """FP8 attention, fp64 result [heads, R, d]: codes [heads * L, d] (head h is
+    rows h*L .. h*L + L - 1), per-tensor fp32 decode scales, softmax scale
+    1/sqrt(d).  Scores are formed as (s_q s_k / sqrt(d)) * sum val(q) val(k) -- the
+    code products and their sum are exact in fp64 -- and V enters as its code
+    values, with s_v applied to the result.  row_idx: query rows within each head
+    (all when None)."""
+    e43 = _table("e4m3")
+    qv = e43[np.asarray(q_codes, np.uint8)]
+    kv = e43[np.asarray(k_codes, np.uint8)]
+    vv = e43[np.asarray(v_codes, np.uint8)]
+    n, d = qv.shape
+    L = n // heads
+    sm = float(np.float64(np.float32(q_scale)) * np.float64(np.float32(k_scale))) / np.sqrt(d)
+    sv = float(np.float32(v_scale))
+    out = []
+    for h in range(heads):
+        qh = qv[h * L:(h + 1) * L]
+        if row_idx is not None:
+            qh = qh[np.asarray(row_idx)]
+        out.append(sv * attention_online(qh, kv[h * L:(h + 1) * L], vv[h * L:(h + 1) * L], sm))
+    return np.stack(out)
+
+
 def max_threads() -> int:
     return _load().orc_max_threads()
 

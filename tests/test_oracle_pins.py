@@ -447,3 +447,87 @@ def test_fp8_weight_gemm_textbook():
     q, s = oracle.quantize_fp8_weight(w, scale=1.0)
     r = oracle.gemm_bf16_fp8w(a, q, s)
     np.testing.assert_array_equal(r, (a_int @ w_int.T).astype(np.float64))
+
+
+# ------------------------------------------------------------------ FP8 attention
+
+def _softmax_attention_two_pass(q, k, v, sm):
+    """Textbook attention in fp64: exact row maximum first, then the normalized
+    probabilities times V (a different order of the same mathematics)."""
+    S = (q @ k.T) * sm
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    return (P / P.sum(axis=1, keepdims=True)) @ v
+
+
+def test_attention_online_equals_two_pass():
+    """Without P quantization the blocked running-maximum algorithm is plain
+    softmax attention: any block size, including 1 and the whole key range, gives
+    the two-pass result (a missing rescale or a stale maximum would not)."""
+    rng = np.random.RandomState(5)
+    q, k, v = rng.randn(7, 16) * 2, rng.randn(200, 16) * 2, rng.randn(200, 16)
+    ref = _softmax_attention_two_pass(q, k, v, 0.37)
+    for block in (1, 7, 64, 200):
+        got = oracle.attention_online(q, k, v, 0.37, block=block, quantize_p=False)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_p_quantizer_worked_values():
+    """q(P) = E4M3 value of P * 256, / 256, worked by hand from the E4M3 grid:
+    0.3 * 256 = 76.8 lies between 72 and 80 (midpoint 76) -> 80; 0.001 * 256 =
+    0.256 lies between 0.25 and 0.28125 (midpoint 0.265625) -> 0.25; 2^-18 * 256 =
+    2^-10 is the midpoint of 0 and the smallest subnormal 2^-9 -> even code 0."""
+    got = oracle.attention_p_quantize(np.array([1.0, 0.3, 0.001, 2.0 ** -18, 0.5, 0.0])) * 256
+    np.testing.assert_array_equal(got, [256.0, 80.0, 0.25, 0.0, 128.0, 0.0])
+
+
+def test_attention_equal_scores_give_the_mean():
+    """All keys equal: every score of a row is the same, P = 1 for every key
+    (encoded exactly), so O is the mean of the V rows."""
+    rng = np.random.RandomState(6)
+    q = rng.randn(5, 8)
+    k = np.tile(rng.randn(1, 8), (130, 1))
+    v = rng.randn(130, 8)
+    got = oracle.attention_online(q, k, v, 0.5)
+    np.testing.assert_allclose(got, np.tile(v.mean(axis=0), (5, 1)), rtol=1e-14, atol=1e-15)
+
+
+def test_attention_dominant_key_selects_its_row():
+    """One key whose score exceeds every other by 40: the others' P * 256 is below
+    2^-17 and encodes to 0, so the numerator is V of that key, and the normalizer
+    1 + sum exp(-40 or less) makes O that row to 1e-16."""
+    d = 8
+    q = np.zeros((1, d))
+    q[0, 0] = 1.0
+    k = np.zeros((150, d))
+    k[97, 0] = 40.0
+    v = np.random.RandomState(7).randn(150, d)
+    got = oracle.attention_online(q, k, v, 1.0)
+    np.testing.assert_allclose(got[0], v[97], rtol=1e-15, atol=1e-15)
+
+
+def test_attention_quantized_error_bound():
+    """Each q(P) is within 2^-4 P of P (E4M3 relative half-step) or below 2^-18 in
+    absolute value, so |O_q - O| <= (2^-4 + 2^-18 L) max|v| per element."""
+    rng = np.random.RandomState(8)
+    q, k, v = rng.randn(9, 32), rng.randn(256, 32), rng.randn(256, 32)
+    exact = _softmax_attention_two_pass(q, k, v, 0.2)
+    quant = oracle.attention_online(q, k, v, 0.2)
+    assert np.abs(quant - exact).max() <= (2.0 ** -4 + 2.0 ** -18 * 256) * np.abs(v).max()
+    assert np.abs(quant - exact).max() > 0          # the quantization is really applied
+
+
+def test_attention_fp8_codes_and_scales():
+    """attention_fp8 forms scores from the code values with s_q s_k / sqrt(d) and
+    applies s_v to the result: the same as attention_online on dequantized
+    operands."""
+    rng = np.random.RandomState(9)
+    heads, L, d = 2, 96, 16
+    bits = [inputs.bf16_bits(rng.randn(heads * L, d)) for _ in range(3)]
+    (qc, qs), (kc, ks), (vc, vs) = [oracle.quantize_fp8_weight(b) for b in bits]
+    e43 = np.array([oracle.code_value(oracle.E4M3, c) for c in range(256)])
+    got = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, heads)
+    for h in range(heads):
+        sl = slice(h * L, (h + 1) * L)
+        ref = oracle.attention_online(e43[qc[sl]] * float(qs), e43[kc[sl]] * float(ks), e43[vc[sl]] * float(vs),
+                                      1.0 / np.sqrt(d))
+        np.testing.assert_allclose(got[h], ref, rtol=1e-12, atol=1e-14)
