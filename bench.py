@@ -329,6 +329,42 @@ def weight_only_fp8_variant(torch, mxq, inputs, wl, reps: int = 20):
     return out
 
 
+def fp8_attention_variant(torch, mxq, inputs, reps: int = 20):
+    """FP8 multi-head attention at FLUX's joint attention shape (24 heads of 128
+    over 4608 tokens): per-tensor E4M3 quantization of Q, K and V (timed apart),
+    then the attention kernel; torch's bf16 scaled_dot_product_attention on the
+    same tensors is timed beside it for context."""
+    heads, L, d = 24, 4608, 128
+    qb, kb, vb = inputs.attention_qkv(heads, L, d, seed=0, stream="bench/attn")
+    q, k, v = (inputs.to_torch(x, "cuda") for x in (qb, kb, vb))
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(3):
+            f()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    qc, qs = mxq.quantize_fp8_weight(q)
+    kc, ks = mxq.quantize_fp8_weight(k)
+    vc, vs = mxq.quantize_fp8_v(v, heads)
+    o = torch.empty((heads * L, d), dtype=torch.bfloat16, device="cuda")
+    a_ms = timed(lambda: mxq.attention_fp8(qc, qs, kc, ks, vc, vs, heads, out=o))
+    q_ms = timed(lambda: (mxq.quantize_fp8_weight(q), mxq.quantize_fp8_weight(k), mxq.quantize_fp8_v(v, heads)))
+    q4, k4, v4 = (x.view(1, heads, L, d) for x in (q, k, v))
+    t_ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q4, k4, v4))
+    flops = 4 * heads * L * L * d
+    rate = flops / (a_ms * 1e-3) / 1e12
+    return {"shape": {"heads": heads, "tokens": L, "head_dim": d}, "flops": flops, "ms": round(a_ms, 4),
+            "TFLOP/s": round(rate, 1), "frac_of_fp8_peak": round(rate / PEAK_TFLOPS["fp8"], 4),
+            "quantize_qkv_ms": round(q_ms, 4), "torch_bf16_sdpa_ms": round(t_ms, 4)}
+
+
 def cpu_baseline(rows_per_linear: int):
     """The oracle (as it is) on a bounded sample: `rows_per_linear` activation rows of
     every linear of the step, quantized (dynamic scales over the sampled rows) and
@@ -508,6 +544,7 @@ def main():
     }
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
+    result["fp8_attention"] = fp8_attention_variant(torch, mxq, inputs)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)

@@ -163,6 +163,45 @@ mxq_status mxq_quantize_fp8_weight(const void* w, int64_t rows, int64_t cols, co
                                    void* stream);
 
 /*
+ * V operand of the FP8 attention [P2 section 2.1: multi-head attention in FP8;
+ * per-tensor E4M3 as for mxq_quantize_fp8_weight].
+ *   v         : bf16 [heads * L, d], device; head h is rows h*L .. h*L + L - 1.
+ *   heads, L, d: heads > 0, d == 128, L a positive multiple of 128, L * 128 < 2^31.
+ *   scale_in, scale_out, workspace: as mxq_quantize_fp8_weight with rows = heads * L,
+ *               cols = d (the scale covers the whole tensor).
+ *   vt        : u8 [heads, 128, L], device, written: the E4M3 codes of V transposed,
+ *               with the columns of every 64-key block b permuted:
+ *               vt[h][c][64 b + 32 g + s] = code(v[h L + 64 b + 32 (s / 16)
+ *                                                   + 8 ((s % 16) / 4) + 4 g + s % 4][c])
+ *               for g in {0, 1}, s in [0, 32) -- the order in which
+ *               mxq_attention_fp8 holds the probabilities of a block.
+ */
+mxq_status mxq_quantize_fp8_v(const void* v, int64_t heads, int64_t L, int64_t d, const float* scale_in,
+                              void* vt, float* scale_out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * FP8 multi-head attention [P2 section 2.1: in the mixed-precision configuration,
+ * multi-head attention runs in FP8], per head, non-causal:
+ *   S = (s_q s_k / sqrt(d)) sum_c val(q[i,c]) val(k[j,c])
+ *   online softmax over key blocks of 64 in key order: m' = max(m, max_j S_ij),
+ *   P_ij = exp(S_ij - m'), l = l exp(m - m') + sum_j P_ij,
+ *   acc = acc exp(m - m') + sum_j val(RN_E4M3(256 P_ij)) val(v[j,:])
+ *   o[i,:] = bf16( s_v acc / (256 l) )
+ * Both products on FP8 matrix cores with fp32 accumulation (exact products).
+ *   q, k      : u8 [heads * L, d] E4M3 codes (mxq_quantize_fp8_weight with
+ *               rows = heads * L), device; q_scale, k_scale their device fp32 scales.
+ *   vt, v_scale: V in the layout of mxq_quantize_fp8_v, and its scale.
+ *   heads, L, d: as mxq_quantize_fp8_v.
+ *   o         : bf16 [heads * L, d], device, written.
+ * Errors: invalid value (null pointer, heads or L not positive), unsupported shape
+ * (d != 128, L not a multiple of 128, L * 128 >= 2^31), misalignment (q, k, vt,
+ * o not 16-byte, scales not 4-byte aligned), device, launch failure.
+ */
+mxq_status mxq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                             const void* vt, const float* v_scale, int64_t heads, int64_t L, int64_t d,
+                             void* o, void* stream);
+
+/*
  * Weight-only FP8 GEMM [P4 sections 3.2 and 4: FP8 weights converted back for a
  * bf16 product ("fake quantization", P5), at a small time cost].
  *   C[m, n] = epi( s_w sum_k a[m,k] val(w_q[n,k]) (+ bias[n]) ), fp32 accumulation,

@@ -35,7 +35,7 @@ _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
            "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size",
-           "mxq_gemm_nvfp4",
+           "mxq_gemm_nvfp4", "mxq_quantize_fp8_v", "mxq_attention_fp8",
            "mxq_gemm_bf16_fp8w", "mxq_status_string", "mxq_last_error"]
 
 
@@ -73,12 +73,15 @@ def load():
         lib.mxq_gemm_nvfp4_workspace_size.argtypes = [i64, i64, i64]
         lib.mxq_gemm_nvfp4_workspace_size.restype = sz
         lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P, sz, P]
+        lib.mxq_quantize_fp8_v.argtypes = [P, i64, i64, i64, P, P, P, P, sz, P]
+        lib.mxq_attention_fp8.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, P]
         lib.mxq_status_string.argtypes = [i32]
         lib.mxq_status_string.restype = ctypes.c_char_p
         lib.mxq_last_error.argtypes = []
         lib.mxq_last_error.restype = ctypes.c_char_p
         for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight",
-                  "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w"):
+                  "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w", "mxq_quantize_fp8_v",
+                  "mxq_attention_fp8"):
             getattr(lib, f).restype = i32
         _lib = lib
         return lib
@@ -288,6 +291,45 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, work
     _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
                               M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes, _stream(stream)))
     return c
+
+
+def quantize_fp8_v(v, heads: int, scale=None, out=None, workspace=None, stream=None):
+    """V of the FP8 attention: bf16 [heads * L, d] (or [heads, L, d]) -> (codes u8
+    [heads, d, L] in the attention's V layout, fp32 per-tensor scale [1])."""
+    torch = _torch()
+    _need(v, torch.bfloat16, "v")
+    d = v.shape[-1]
+    L = v.numel() // (heads * d)
+    q, s_out = out if out is not None else (torch.empty((heads, d, L), dtype=torch.uint8, device=v.device),
+                                            torch.empty((1,), dtype=torch.float32, device=v.device))
+    lib = load()
+    ws, nbytes = None, 0
+    if scale is None:
+        nbytes = int(lib.mxq_quantize_nvfp4_workspace_size(heads * L, d))
+        ws = workspace if workspace is not None else torch.empty((max(nbytes, 4),), dtype=torch.uint8,
+                                                                 device=v.device)
+        nbytes = ws.numel()
+    _check(lib.mxq_quantize_fp8_v(_ptr(v), heads, L, d, _ptr(scale), _ptr(q), _ptr(s_out), _ptr(ws), nbytes,
+                                  _stream(stream)))
+    return q, s_out
+
+
+def attention_fp8(q, q_scale, k, k_scale, vt, v_scale, heads: int, out=None, stream=None):
+    """FP8 multi-head attention: E4M3 codes q, k [heads * L, d], V in the layout of
+    quantize_fp8_v, fp32 scales [1] -> bf16 [heads * L, d]."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.uint8, n)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, torch.float32, n)
+    d = q.shape[-1]
+    L = q.numel() // (heads * d)
+    if k.numel() != q.numel() or vt.numel() != q.numel():
+        raise ValueError("q, k, vt sizes disagree")
+    o = out if out is not None else torch.empty((heads * L, d), dtype=torch.bfloat16, device=q.device)
+    _check(load().mxq_attention_fp8(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(vt), _ptr(v_scale),
+                                    heads, L, d, _ptr(o), _stream(stream)))
+    return o
 
 
 def gemm_bf16_fp8w(a, w_q, w_scale, bias=None, epi=None, out=None, stream=None):

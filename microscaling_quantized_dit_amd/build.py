@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxq.so")
 SOURCES = ["quant_mxfp8.hip", "quant_nvfp4.hip", "gemm_mxfp8.hip", "gemm_nvfp4.hip", "gemm_w8.hip", "gemm_fixup.hip",
-           "mxq_api.cpp"]
+           "attention_fp8.hip", "mxq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

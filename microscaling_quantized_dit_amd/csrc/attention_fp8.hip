@@ -1,0 +1,223 @@
+// FP8 multi-head attention for gfx950 (page "NVIDIA Blackwell平台FP4量化技术解析与图像
+// 生成优化", section 2.1: the mixed-precision configuration runs multi-head
+// attention in FP8).  Per head, with head dimension 128:
+//   S = (s_q s_k / sqrt(128)) Q_c K_c^T          Q_c, K_c: per-tensor E4M3 codes
+//   online softmax over key blocks of 64, in key order: m' = max(m, max_j S_j),
+//   P_j = exp(S_j - m'), l = l e^(m - m') + sum_j P_j,
+//   acc = acc e^(m - m') + sum_j val(RN_E4M3(256 P_j)) V_c[j]
+//   O = s_v acc / (256 l)                       (bf16, one rounding)
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
+// scales): exact products, fp32 accumulation.
+//
+// Layout.  S is computed transposed, S^T = K Q^T (K the first operand), so that
+// lane l holds query l % 32 and, per 32-key tile t, the 16 keys
+// 32t + 8(v/4) + 4g + v%4 (g = l / 32, v = 0..15): the softmax of a query stays in
+// one lane pair (l, l + 32).  Its probabilities, as E4M3 codes in slot order
+// s = 16t + v, are directly the second operand of O^T = V^T P^T; V comes in the
+// layout k_quant_fp8_vt writes (transposed, each 64-key block's columns permuted so
+// that column 32g + s holds the key of slot s), so the first operand is 32
+// consecutive bytes of a V^T row.  O^T puts the 128 output columns of the lane's
+// query in its accumulators (16 per 32-column tile and lane group).
+//
+// Work: one workgroup of 4 waves per 128 queries of a head (32 queries per wave);
+// K and V blocks of 64 keys go global -> LDS by buffer_load ... lds into two
+// buffers (XOR-swizzled rows: conflict-free reads), the next block landing while
+// the current one is used; Q stays in registers.
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kThreads = 256;
+constexpr int kD = 128;                 // head dimension
+constexpr int kQB = 128;                // queries per workgroup
+constexpr int kKB = 64;                 // keys per block
+constexpr int kKBytes = kKB * kD;       // K block: 64 rows of 128 code bytes
+constexpr int kVBytes = kD * kKB;       // V^T block: 128 rows of 64 code bytes
+
+// K rows (8 chunks of 16 B) keep logical chunk c at c ^ swz_k(row); V^T rows (4
+// chunks) at c ^ swz_v(row): the 16 rows of a quarter-wave read then cover 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int row) { return (row >> 2) & 3; }
+
+__device__ __forceinline__ v8i cat(uint4 a, uint4 b) {
+  return v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// E4M3 x E4M3, 32x32x64, unit scales (E8M0 127)
+__device__ __forceinline__ v16f mfma8(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __restrict__ q,
+                                                               const uint8_t* __restrict__ k,
+                                                               const uint8_t* __restrict__ vt,
+                                                               const float* __restrict__ qs,
+                                                               const float* __restrict__ ks,
+                                                               const float* __restrict__ vs,
+                                                               uint16_t* __restrict__ o, int L) {
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1[kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0[kVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1[kVBytes];
+
+  const int head = blockIdx.y, q0 = blockIdx.x * kQB;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int r = lane & 31, g = lane >> 5;
+  const int nkb = L / kKB;                  // even: L is a multiple of 128
+
+  // this head's K [L][128] and V^T [128][L]; byte offsets < 2^31 (checked by the host)
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + (size_t)head * L * kD), (short)0, L * kD,
+                                                    0x00020000);
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vt + (size_t)head * kD * L), (short)0, kD * L,
+                                                    0x00020000);
+
+  // Global -> LDS, 1 KiB per wave and load.  K: wave w fills rows 16w..16w+15 in two
+  // loads of 8 rows x 128 B (lane i -> row i / 8, physical chunk i % 8; rows 8j + i/8
+  // have swizzle ((i/8) >> 1) + 4j).  V^T: rows 32w..32w+31 in two loads of 16 rows
+  // x 64 B (lane i -> row i / 4, physical chunk i % 4, swizzle (i >> 4) & 3).
+  const int krow = lane >> 3, kcx = (lane & 7) ^ (krow >> 1);
+  const int vok0 = krow * kD + kcx * 16, vok1 = krow * kD + (kcx ^ 4) * 16;
+  const int vov = (lane >> 2) * L + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  auto dma = [&](uint8_t* kb, uint8_t* vb, int blk) {
+    const int key0 = blk * kKB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kb + 16 * wave * kD), 16, vok0,
+                                             (key0 + 16 * wave) * kD, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kb + (16 * wave + 8) * kD), 16, vok1,
+                                             (key0 + 16 * wave + 8) * kD, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vb + 32 * wave * kKB), 16, vov,
+                                             32 * wave * L + key0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vb + (32 * wave + 16) * kKB), 16, vov,
+                                             (32 * wave + 16) * L + key0, 0, 0);
+  };
+
+  // K operand of key tile tt, head-dimension half hd: row 32tt + r, chunks 4hd + g
+  // and 4hd + 2 + g (bytes 16g.. and 32 + 16g.. of the half)
+  const int xk = swz_k(r), xv = swz_v(r);   // 32tt + r and 32dt + r share them
+  auto kfrag = [&](const uint8_t* kb, int tt, int hd) {
+    const uint8_t* p = kb + (32 * tt + r) * kD;
+    return cat(*(const uint4*)(p + (((4 * hd + g) ^ xk) << 4)), *(const uint4*)(p + (((4 * hd + 2 + g) ^ xk) << 4)));
+  };
+  // V^T operand of output-column tile dt: row 32dt + r, bytes [32g, 32g + 32)
+  auto vfrag = [&](const uint8_t* vb, int dt) {
+    const uint8_t* p = vb + (32 * dt + r) * kKB;
+    return cat(*(const uint4*)(p + (((2 * g) ^ xv) << 4)), *(const uint4*)(p + (((2 * g + 1) ^ xv) << 4)));
+  };
+
+  // Q operand (this lane's query, both halves of the head dimension), in registers
+  const uint8_t* qrow = q + ((size_t)head * L + q0 + 32 * wave + r) * kD;
+  v8i qf[2];
+#pragma unroll
+  for (int hd = 0; hd < 2; ++hd)
+    qf[hd] = cat(*(const uint4*)(qrow + 64 * hd + 16 * g), *(const uint4*)(qrow + 64 * hd + 32 + 16 * g));
+
+  // scores in the log2 domain: x = S log2(e)
+  const float c2 = (*qs) * (*ks) * (0.08838834764831845f * 1.4426950408889634f);
+  float m_run = -__builtin_inff(), l_run = 0.0f;   // l_run: this lane group's keys only
+  v16f acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[dt][v] = 0.0f;
+
+  auto block = [&](const uint8_t* kb, const uint8_t* vb) {
+    v16f s[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[tt][v] = 0.0f;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) s[tt] = mfma8(kfrag(kb, tt, hd), qf[hd], s[tt]);
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[tt][v] *= c2;
+        mx = fmaxf(mx, s[tt][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));        // the query's other 32 keys
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
+    m_run = m_new;
+    float psum = 0.0f;
+    uint32_t pw[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = __builtin_amdgcn_exp2f(s[tt][4 * vq + u] - m_new);
+          psum += p[u];
+        }
+        // codes of 256 P (exact scaling; at most 256, below E4M3's saturation)
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.0f, p[1] * 256.0f, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.0f, p[3] * 256.0f, w, true);
+        pw[4 * tt + vq] = (uint32_t)w;
+      }
+    l_run = l_run * alpha + psum;
+    const v8i pb = v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
+      acc[dt] = mfma8(vfrag(vb, dt), pb, acc[dt]);
+    }
+  };
+
+  // Prologue: blocks 0 and 1 in flight, wait for both.  Then block b uses buffer
+  // b & 1; after it every wave waits for block b + 1 and for its own LDS reads, and
+  // at the barrier buffer b & 1 is free for block b + 2.
+  dma(k0, v0, 0);
+  dma(k1, v1, 1);
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
+  __syncthreads();
+  for (int b = 0; b < nkb; b += 2) {
+    block(k0, v0);
+    __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    __syncthreads();
+    if (b + 2 < nkb) dma(k0, v0, b + 2);
+    block(k1, v1);
+    __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    __syncthreads();
+    if (b + 3 < nkb) dma(k1, v1, b + 3);
+  }
+
+  // O = s_v acc / (256 l): lane (r, g) holds columns 32dt + 8vq + 4g + u of its query
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float f = (*vs) * (1.0f / 256.0f) / l_tot;
+  uint16_t* orow = o + ((size_t)head * L + q0 + 32 * wave + r) * kD + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq) {
+      uint2 w;
+      w.x = dev::pack_bf16x2(acc[dt][4 * vq] * f, acc[dt][4 * vq + 1] * f);
+      w.y = dev::pack_bf16x2(acc[dt][4 * vq + 2] * f, acc[dt][4 * vq + 3] * f);
+      *(uint2*)(orow + 32 * dt + 8 * vq) = w;
+    }
+}
+
+}  // namespace
+
+// Shapes reaching here are validated: head dimension 128, L a positive multiple of
+// 128 with L * 128 < 2^31, heads > 0.
+hipError_t launch_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                const void* vt, const float* v_scale, int64_t heads, int64_t L, void* o,
+                                hipStream_t stream) {
+  dim3 grid((unsigned)(L / kQB), (unsigned)heads), block(kThreads);
+  hipLaunchKernelGGL(k_attention_fp8, grid, block, 0, stream, (const uint8_t*)q, (const uint8_t*)k,
+                     (const uint8_t*)vt, q_scale, k_scale, v_scale, (uint16_t*)o, (int)L);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -164,6 +164,53 @@ mxq_status mxq_quantize_fp8_weight(const void* w, int64_t rows, int64_t cols, co
                   "mxq_quantize_fp8_weight launch");
 }
 
+static mxq_status check_attention_shape(int64_t heads, int64_t L, int64_t d) {
+  if (heads <= 0 || L <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "heads and L must be positive");
+  if (d != 128) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "head dimension %lld (only 128)", (long long)d);
+  if (L % 128 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "L (%lld) must be a multiple of 128", (long long)L);
+  if (L >= kMax32 / 128) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "L * 128 must be < 2^31");
+  if (heads > INT32_MAX / 2 || heads > INT64_MAX / (L * 128)) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "too many heads");
+  return MXQ_SUCCESS;
+}
+
+mxq_status mxq_quantize_fp8_v(const void* v, int64_t heads, int64_t L, int64_t d, const float* scale_in, void* vt,
+                              float* scale_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!v || !vt || !scale_out) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  mxq_status s = check_attention_shape(heads, L, d);
+  if (s != MXQ_SUCCESS) return s;
+  if (!aligned16(v) || !aligned16(vt)) return fail(MXQ_ERROR_MISALIGNED, "v and vt must be 16-byte aligned");
+  if (((uintptr_t)scale_out & 3u) || ((uintptr_t)scale_in & 3u))
+    return fail(MXQ_ERROR_MISALIGNED, "scale pointers must be 4-byte aligned");
+  if (!scale_in) {
+    const size_t need = mxq_quantize_nvfp4_workspace_size(heads * L, d);
+    if (!workspace || ws_bytes < need)
+      return fail(MXQ_ERROR_WORKSPACE, "dynamic mode needs a %zu-byte workspace (got %zu)", need,
+                  workspace ? ws_bytes : (size_t)0);
+    if ((uintptr_t)workspace & 3u) return fail(MXQ_ERROR_MISALIGNED, "workspace must be 4-byte aligned");
+  }
+  mxq_status dv = check_device();
+  if (dv != MXQ_SUCCESS) return dv;
+  return launched(mxq::launch_quantize_fp8_vt(v, heads, L, scale_in, vt, scale_out, (uint32_t*)workspace,
+                                              (hipStream_t)stream),
+                  "mxq_quantize_fp8_v launch");
+}
+
+mxq_status mxq_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale, const void* vt,
+                             const float* v_scale, int64_t heads, int64_t L, int64_t d, void* o, void* stream) {
+  if (!q || !q_scale || !k || !k_scale || !vt || !v_scale || !o)
+    return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  mxq_status s = check_attention_shape(heads, L, d);
+  if (s != MXQ_SUCCESS) return s;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+    return fail(MXQ_ERROR_MISALIGNED, "q, k, vt and o must be 16-byte aligned");
+  if (((uintptr_t)q_scale & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_scale & 3u))
+    return fail(MXQ_ERROR_MISALIGNED, "scale pointers must be 4-byte aligned");
+  mxq_status dv = check_device();
+  if (dv != MXQ_SUCCESS) return dv;
+  return launched(mxq::launch_attention_fp8(q, q_scale, k, k_scale, vt, v_scale, heads, L, o, (hipStream_t)stream),
+                  "mxq_attention_fp8 launch");
+}
+
 static mxq_status check_gemm_common(int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c,
                                     int64_t a_row_bytes_num, int64_t a_row_bytes_den) {
   if (!c) return fail(MXQ_ERROR_INVALID_VALUE, "null output pointer");

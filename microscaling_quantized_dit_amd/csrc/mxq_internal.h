@@ -51,6 +51,17 @@ size_t gemm_split_bytes(const GemmSplit& sp, int tiles);
 hipError_t launch_gemm_fixup(const GemmSplit& sp, int64_t M, int64_t N, const float* alpha_a, const float* alpha_b,
                              const void* bias, int epi, void* c, hipStream_t stream);
 
+// V of the FP8 attention: [heads * L, 128] bf16 -> codes in the attention's V
+// layout (see k_quant_fp8_vt); partials as for the quantizers (scale_in NULL).
+hipError_t launch_quantize_fp8_vt(const void* v, int64_t heads, int64_t L, const float* scale_in, void* vt,
+                                  float* scale_out, uint32_t* partials, hipStream_t stream);
+
+// FP8 attention: q, k codes [heads * L, 128], vt in the V layout, per-tensor
+// decode scales, o bf16 [heads * L, 128]; L a multiple of 128.
+hipError_t launch_attention_fp8(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                const void* vt, const float* v_scale, int64_t heads, int64_t L, void* o,
+                                hipStream_t stream);
+
 hipError_t launch_gemm_w8(const void* a, const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
                           const void* bias, int epi, void* c, hipStream_t stream);
 

@@ -250,13 +250,77 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   }
 }
 
-// Per-tensor FP8 weights (page "麦橘超然性能实战分析：float8量化如何提升GPU利用率",
-// section 3.2: DiT weights held as float8_e4m3fn; page "FP8量化技术提升SD3.5在低带宽
-// 环境下的响应速度", step 2: q = round(w / scale)):
+// Per-tensor E4M3 encoding, shared by the weight quantizer and the attention's V
+// quantizer (page "麦橘超然性能实战分析：float8量化如何提升GPU利用率", section 3.2:
+// DiT weights held as float8_e4m3fn; page "FP8量化技术提升SD3.5在低带宽环境下的响应速度",
+// step 2: q = round(w / scale)):
 //   s = RN_fp32(amax / 448) (1 for an all-zero tensor; or given), q = RN_E4M3_sat(w / s).
-// Eight values per lane (one uint4 of bf16 -> one uint2 of codes).  The quotient is
-// bracketed like the NVFP4 codes; a near tie is settled by round_up_at against the
-// midpoint of the two candidate codes; an extreme s takes the fp64 search.
+// The quotient is bracketed like the NVFP4 codes; a near tie is settled by
+// round_up_at against the midpoint of the two candidate codes; an extreme s takes
+// the fp64 search.
+struct E4M3Encoder {
+  float sw, r_lo, r_hi;
+  bool fast;
+};
+
+// The decode scale: given, or RN_fp32(amax / 448) from the amax pass's partial
+// maxima (every thread of the workgroup calls this; red holds 4 words of LDS).
+__device__ __forceinline__ E4M3Encoder e4m3_encoder(const float* scale_in, const uint32_t* partials, int n_partials,
+                                                    uint32_t* red) {
+  E4M3Encoder enc;
+  const int t = threadIdx.x;
+  if (scale_in) {
+    enc.sw = *scale_in;
+  } else {
+    uint32_t m = t < n_partials ? partials[t] : 0u;
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    const uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    enc.sw = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 448.0f;   // IEEE division
+  }
+  const double rd = 1.0 / (double)enc.sw;
+  enc.r_lo = (float)(rd * (1.0 - 0x1p-19));
+  enc.r_hi = (float)(rd * (1.0 + 0x1p-19));
+  // fp32 brackets and the two-product test need sw and 1/sw well inside fp32's range
+  enc.fast = rd < 0x1p126 && rd > 0x1p-126 && enc.sw >= 0x1p-100f;
+  return enc;
+}
+
+// Four values (exact fp32 of bf16 inputs) -> four E4M3 codes, byte e = xs[e].
+__device__ __forceinline__ uint32_t encode_e4m3x4(const E4M3Encoder& enc, const float (&xs)[4]) {
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * enc.r_lo, -448.0f, 448.0f),
+                                       __builtin_amdgcn_fmed3f(xs[1] * enc.r_lo, -448.0f, 448.0f), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * enc.r_lo, -448.0f, 448.0f),
+                                       __builtin_amdgcn_fmed3f(xs[3] * enc.r_lo, -448.0f, 448.0f), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * enc.r_hi, -448.0f, 448.0f),
+                                       __builtin_amdgcn_fmed3f(xs[1] * enc.r_hi, -448.0f, 448.0f), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * enc.r_hi, -448.0f, 448.0f),
+                                       __builtin_amdgcn_fmed3f(xs[3] * enc.r_hi, -448.0f, 448.0f), hi, true);
+  uint32_t codes = (uint32_t)lo;
+  if (__builtin_expect(!enc.fast, 0)) {
+    codes = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t mag = (uint32_t)exact_block_scale((double)fabsf(xs[e]), (double)enc.sw);
+      codes |= (mag | (__float_as_uint(xs[e]) >> 31 << 7)) << (8 * e);
+    }
+  } else if (__builtin_expect(codes != (uint32_t)hi, 0)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t cl = (codes >> (8 * e)) & 0x7Fu, ch = ((uint32_t)hi >> (8 * e)) & 0x7Fu;
+      if (cl != ch) {
+        const float mk = (__builtin_amdgcn_cvt_f32_fp8((int)cl, 0) + __builtin_amdgcn_cvt_f32_fp8((int)ch, 0)) * 0.5f;
+        const uint32_t mag = round_up_at(fabsf(xs[e]), mk, enc.sw, (ch & 1) == 0) ? ch : cl;
+        codes = (codes & ~(0x7Fu << (8 * e))) | (mag << (8 * e));
+      }
+    }
+  }
+  return codes;
+}
+
+// Per-tensor FP8 weights: eight values per lane (one uint4 of bf16 -> one uint2 of codes).
 __global__ __launch_bounds__(kThreads) void k_quant_fp8_tensor(const uint4* __restrict__ x, int64_t n_chunks,
                                                                const float* __restrict__ scale_in,
                                                                const uint32_t* __restrict__ partials,
@@ -271,23 +335,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_tensor(const uint4* __re
     const int64_t c = base + u * kThreads + t;
     v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
   }
-  float sw;
-  if (scale_in) {
-    sw = *scale_in;
-  } else {
-    uint32_t m = t < n_partials ? partials[t] : 0u;
-    m = wave_max(m);
-    if ((t & 63) == 0) red[t >> 6] = m;
-    __syncthreads();
-    const uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
-    sw = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 448.0f;   // IEEE division
-  }
-  if (blockIdx.x == 0 && t == 0) *scale_out = sw;
-  const double rd = 1.0 / (double)sw;
-  const float r_lo = (float)(rd * (1.0 - 0x1p-19)), r_hi = (float)(rd * (1.0 + 0x1p-19));
-  // fp32 brackets and the two-product test need sw and 1/sw well inside fp32's range
-  const bool fast = rd < 0x1p126 && rd > 0x1p-126 && sw >= 0x1p-100f;
-
+  const E4M3Encoder enc = e4m3_encoder(scale_in, partials, n_partials, red);
+  if (blockIdx.x == 0 && t == 0) *scale_out = enc.sw;
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t c = base + u * kThreads + t;
@@ -295,42 +344,52 @@ __global__ __launch_bounds__(kThreads) void k_quant_fp8_tensor(const uint4* __re
     uint32_t out[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // four values -> four codes, for each bracket
-      int lo = 0, hi = 0;
       float xs[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) xs[e] = (e & 1) ? dev::bf16_hi(w[2 * h + (e >> 1)]) : dev::bf16_lo(w[2 * h + (e >> 1)]);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * r_lo, -448.0f, 448.0f),
-                                           __builtin_amdgcn_fmed3f(xs[1] * r_lo, -448.0f, 448.0f), lo, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * r_lo, -448.0f, 448.0f),
-                                           __builtin_amdgcn_fmed3f(xs[3] * r_lo, -448.0f, 448.0f), lo, true);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[0] * r_hi, -448.0f, 448.0f),
-                                           __builtin_amdgcn_fmed3f(xs[1] * r_hi, -448.0f, 448.0f), hi, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(xs[2] * r_hi, -448.0f, 448.0f),
-                                           __builtin_amdgcn_fmed3f(xs[3] * r_hi, -448.0f, 448.0f), hi, true);
-      uint32_t codes = (uint32_t)lo;
-      if (__builtin_expect(!fast, 0)) {
-        codes = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t mag = (uint32_t)exact_block_scale((double)fabsf(xs[e]), (double)sw);
-          codes |= (mag | (__float_as_uint(xs[e]) >> 31 << 7)) << (8 * e);
-        }
-      } else if (__builtin_expect(codes != (uint32_t)hi, 0)) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t cl = (codes >> (8 * e)) & 0x7Fu, ch = ((uint32_t)hi >> (8 * e)) & 0x7Fu;
-          if (cl != ch) {
-            const float mk = (__builtin_amdgcn_cvt_f32_fp8((int)cl, 0) + __builtin_amdgcn_cvt_f32_fp8((int)ch, 0)) * 0.5f;
-            const uint32_t mag = round_up_at(fabsf(xs[e]), mk, sw, (ch & 1) == 0) ? ch : cl;
-            codes = (codes & ~(0x7Fu << (8 * e))) | (mag << (8 * e));
-          }
-        }
-      }
-      out[h] = codes;
+      out[h] = encode_e4m3x4(enc, xs);
     }
     if (c < n_chunks) q[c] = make_uint2(out[0], out[1]);
   }
+}
+
+// V of the FP8 attention: [heads * L, 128] bf16 -> per-tensor E4M3 codes in the
+// attention kernel's V layout, [heads][128][L] (V transposed, so that a row holds
+// one output column over the keys), with the columns of every 64-key block
+// permuted: column 32g + s holds key 32 (s / 16) + 8 ((s % 16) / 4) + 4g + s % 4.
+// That is the key whose probability lane group g of the score MFMA holds in its
+// register slot s, so the P.V operands pair up byte for byte.  One workgroup per
+// 64-key block of a head: the bf16 block through LDS, then 32 codes per thread.
+__global__ __launch_bounds__(kThreads) void k_quant_fp8_vt(const uint16_t* __restrict__ v, int L,
+                                                           const float* __restrict__ scale_in,
+                                                           const uint32_t* __restrict__ partials, int n_partials,
+                                                           uint8_t* __restrict__ vt, float* __restrict__ scale_out) {
+  constexpr int kRow = 136;                       // bf16 per staged key row (128 + 8 of padding)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kRow];
+  __shared__ uint32_t red[kThreads / 64];
+  const int t = threadIdx.x, kb = blockIdx.x, head = blockIdx.y;
+  const uint16_t* src = v + ((size_t)head * L + kb * 64 + t / 4) * 128 + (t % 4) * 32;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) *(uint4*)(tile + (t / 4) * kRow + (t % 4) * 32 + 8 * u) = ((const uint4*)src)[u];
+  const E4M3Encoder enc = e4m3_encoder(scale_in, partials, n_partials, red);
+  if (kb == 0 && head == 0 && t == 0) *scale_out = enc.sw;
+  __syncthreads();
+  const int e = t >> 1, g = t & 1;
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float xs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sl = 4 * w + u;
+      const int key = 32 * (sl / 16) + 8 * ((sl % 16) / 4) + 4 * g + sl % 4;
+      xs[u] = __uint_as_float((uint32_t)tile[key * kRow + e] << 16);
+    }
+    out[w] = encode_e4m3x4(enc, xs);
+  }
+  uint4* dst = (uint4*)(vt + ((size_t)head * 128 + e) * L + kb * 64 + 32 * g);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
 // Calibration fold: running = max(running, RN_fp32(amax / 2688)) over the partial
@@ -369,6 +428,22 @@ hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const floa
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_quant_fp8_tensor, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x, n_chunks,
                      scale_in, partials, n_partials, (uint2*)q, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_vt(const void* v, int64_t heads, int64_t L, const float* scale_in, void* vt,
+                                  float* scale_out, uint32_t* partials, hipStream_t stream) {
+  const int64_t n_elems = heads * L * 128;
+  int n_partials = 0;
+  if (!scale_in) {
+    n_partials = nvfp4_amax_partials(n_elems);
+    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)v,
+                       n_elems / 8, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_quant_fp8_vt, dim3((unsigned)(L / 64), (unsigned)heads), dim3(kThreads), 0, stream,
+                     (const uint16_t*)v, (int)L, scale_in, partials, n_partials, (uint8_t*)vt, scale_out);
   return hipGetLastError();
 }
 

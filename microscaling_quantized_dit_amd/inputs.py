@@ -19,7 +19,11 @@ trained weights they use are not available, so these seeded tensors stand in):
     round(0.001 * numel) distinct seeded positions) multiplied by 50;
   * the tiny case: N(0, 1) with 1% outliers x20, weights N(0, 0.02);
   * long-sequence case: N(0, 1) with 0.1% outliers x50;
-  * weights N(0, 1/sqrt(K)); bias N(0, 1/sqrt(K)).
+  * weights N(0, 1/sqrt(K)); bias N(0, 1/sqrt(K));
+  * attention (FLUX joint attention: 24 heads of dimension 128 over the 4608
+    tokens): Q and K N(0, gain) -- FLUX normalizes q and k per head (RMSNorm),
+    so unit scale is the plain stand-in, gain > 1 sharpens the softmax -- and
+    V N(0, 1), each [heads * L, 128] with head h in rows h*L .. h*L + L - 1.
 Standard deviations are the second argument of N(., .).
 """
 from __future__ import annotations
@@ -190,6 +194,14 @@ def weight(n: int, k: int, seed: int = 0, stream: str = "W", std: float | None =
 
 def bias(n: int, k: int, seed: int = 0, stream: str = "bias") -> np.ndarray:
     return gaussian(1, n, 1.0 / np.sqrt(k), seed, stream).reshape(n)
+
+
+def attention_qkv(heads: int, L: int, d: int = 128, seed: int = 0, stream: str = "attn", gain: float = 1.0):
+    """bf16 (Q, K, V), each [heads * L, d]: Q, K ~ N(0, gain), V ~ N(0, 1)."""
+    q = gaussian(heads * L, d, gain, seed, stream + "/Q")
+    k = gaussian(heads * L, d, gain, seed, stream + "/K")
+    v = gaussian(heads * L, d, 1.0, seed, stream + "/V")
+    return q, k, v
 
 
 def to_torch(bits: np.ndarray, device=None):

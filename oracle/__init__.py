@@ -306,10 +306,12 @@ def attention_p_quantize(p: np.ndarray) -> np.ndarray:
     return (_table("e4m3")[codes] / ATTN_P_SCALE).reshape(p.shape)
 
 
-def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize_p: bool = True) -> np.ndarray:
+def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize_p: bool = True,
+                     return_l: bool = False):
     """Online-softmax attention of fp64 rows q [R, d] over k, v [L, d]:
     acc / l as above, with scores S = sm_scale * q . k.  quantize_p=False keeps P
-    unquantized (plain softmax attention, computed blockwise)."""
+    unquantized (plain softmax attention, computed blockwise).  return_l: also
+    the final normalizer l = sum_j exp(S_j - max S) per row."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -326,16 +328,17 @@ def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize
         Pq = attention_p_quantize(P) if quantize_p else P
         acc = acc * alpha[:, None] + Pq @ v[b0:b0 + block]
         m = m_new
-    return acc / l[:, None]
+    return (acc / l[:, None], l) if return_l else acc / l[:, None]
 
 
-def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: int, row_idx=None) -> np.ndarray:
+def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: int, row_idx=None,
+                  return_l: bool = False):
     """FP8 attention, fp64 result [heads, R, d]: codes [heads * L, d] (head h is
     rows h*L .. h*L + L - 1), per-tensor fp32 decode scales, softmax scale
     1/sqrt(d).  Scores are formed as (s_q s_k / sqrt(d)) * sum val(q) val(k) -- the
     code products and their sum are exact in fp64 -- and V enters as its code
     values, with s_v applied to the result.  row_idx: query rows within each head
-    (all when None)."""
+    (all when None).  return_l: also the normalizers [heads, R]."""
     e43 = _table("e4m3")
     qv = e43[np.asarray(q_codes, np.uint8)]
     kv = e43[np.asarray(k_codes, np.uint8)]
@@ -344,13 +347,15 @@ def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: i
     L = n // heads
     sm = float(np.float64(np.float32(q_scale)) * np.float64(np.float32(k_scale))) / np.sqrt(d)
     sv = float(np.float32(v_scale))
-    out = []
+    out, ls = [], []
     for h in range(heads):
         qh = qv[h * L:(h + 1) * L]
         if row_idx is not None:
             qh = qh[np.asarray(row_idx)]
-        out.append(sv * attention_online(qh, kv[h * L:(h + 1) * L], vv[h * L:(h + 1) * L], sm))
-    return np.stack(out)
+        o, l = attention_online(qh, kv[h * L:(h + 1) * L], vv[h * L:(h + 1) * L], sm, return_l=True)
+        out.append(sv * o)
+        ls.append(l)
+    return (np.stack(out), np.stack(ls)) if return_l else np.stack(out)
 
 
 def max_threads() -> int:

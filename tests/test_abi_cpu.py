@@ -38,8 +38,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_quantize_nvfp4_workspace_size",
-              "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size", "mxq_gemm_nvfp4", "mxq_status_string",
-              "mxq_last_error"]:
+              "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size", "mxq_gemm_nvfp4", "mxq_quantize_fp8_v",
+              "mxq_attention_fp8", "mxq_status_string", "mxq_last_error"]:
         assert s in syms
 
 
@@ -168,6 +168,27 @@ def test_gemm_nvfp4_validation(lib):
     assert lib.mxq_gemm_nvfp4_workspace_size(4096, 4096, 1024) == 0    # 256 tiles: one full round
     assert lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1152) == 0    # odd stage count: no persistence
     assert lib.mxq_gemm_nvfp4_workspace_size(100, 4096, 1024) == 0
+
+
+def test_attention_validation(lib):
+    def att(q=FAKE, qs=FAKE, heads=2, L=256, d=128, o=FAKE):
+        return lib.mxq_attention_fp8(q, qs, FAKE, FAKE, FAKE, FAKE, heads, L, d, o, None)
+
+    def vq(v=FAKE, heads=2, L=256, d=128, scale=None, ws=FAKE, nbytes=1 << 20):
+        return lib.mxq_quantize_fp8_v(v, heads, L, d, scale, FAKE, FAKE, ws, nbytes, None)
+
+    assert att(q=None) == INVALID
+    assert att(heads=0) == INVALID
+    assert att(d=64) == SHAPE
+    assert att(L=192) == SHAPE                     # multiple of 128
+    assert att(L=1 << 24) == SHAPE                 # L * 128 must stay below 2^31
+    assert att(o=FAKE + 2) == MISALIGNED
+    assert att(qs=FAKE + 2) == MISALIGNED
+    assert vq(v=None) == INVALID
+    assert vq(d=256) == SHAPE
+    assert vq(ws=None) == WORKSPACE                # dynamic scale needs the partials
+    assert vq(nbytes=4) == WORKSPACE
+    assert vq(v=FAKE + 8) == MISALIGNED
 
 
 @pytest.mark.skipif(gpu_available(), reason="device gate is only observable without a GPU")
