@@ -117,9 +117,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
   for (int hd = 0; hd < 2; ++hd)
     qf[hd] = cat(*(const uint4*)(qrow + 64 * hd + 16 * g), *(const uint4*)(qrow + 64 * hd + 32 + 16 * g));
 
-  // scores in the log2 domain: x = S log2(e)
+  // scores in the log2 domain: x = S log2(e) = c2 * (sum of code products)
   const float c2 = (*qs) * (*ks) * (0.08838834764831845f * 1.4426950408889634f);
-  float m_run = -__builtin_inff(), l_run = 0.0f;   // l_run: this lane group's keys only
+  // running maximum of x; l_run = 256 * (sum of P) over this lane group's keys
+  float m_run = -__builtin_inff(), l_run = 0.0f;
   v16f acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -135,18 +136,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd) s[tt] = mfma8(kfrag(kb, tt, hd), qf[hd], s[tt]);
     }
-    float mx = -__builtin_inff();
+    // block maximum on the raw sums (c2 > 0 keeps the order; rounding is monotone)
+    float mraw = -__builtin_inff();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[tt][v] *= c2;
-        mx = fmaxf(mx, s[tt][v]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));        // the query's other 32 keys
-    const float m_new = fmaxf(m_run, mx);
+      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, s[tt][v]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));   // the query's other 32 keys
+    const float m_new = fmaxf(m_run, mraw * c2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
     m_run = m_new;
+    // 256 P = 2^(x - m + 8), with the scaling, the offset and the factor 256 in one fma
+    const float off = 8.0f - m_new;
     float psum = 0.0f;
     uint32_t pw[8];
 #pragma unroll
@@ -156,12 +157,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
         float p[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          p[u] = __builtin_amdgcn_exp2f(s[tt][4 * vq + u] - m_new);
+          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][4 * vq + u], c2, off));
           psum += p[u];
         }
-        // codes of 256 P (exact scaling; at most 256, below E4M3's saturation)
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.0f, p[1] * 256.0f, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.0f, p[3] * 256.0f, w, true);
+        // E4M3 codes of 256 P (at most 256: below E4M3's saturation)
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[4 * tt + vq] = (uint32_t)w;
       }
     l_run = l_run * alpha + psum;
@@ -192,9 +193,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
     if (b + 3 < nkb) dma(k1, v1, b + 3);
   }
 
-  // O = s_v acc / (256 l): lane (r, g) holds columns 32dt + 8vq + 4g + u of its query
+  // O = s_v acc / (256 l) = s_v acc / l_tot (l_run counts 256 P): lane (r, g) holds
+  // columns 32dt + 8vq + 4g + u of its query
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float f = (*vs) * (1.0f / 256.0f) / l_tot;
+  const float f = (*vs) / l_tot;
   uint16_t* orow = o + ((size_t)head * L + q0 + 32 * wave + r) * kD + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
