@@ -81,8 +81,11 @@ KERNEL_SOURCES = {  # HIP kernel -> sources whose text decides its code
     "k_amax_partials": ["quant_nvfp4.hip"],
     "k_quant_nvfp4": ["quant_nvfp4.hip"],
     "k_gemm_mxfp8": ["gemm_mxfp8.hip"],
-    "k_gemm_nvfp4": ["gemm_nvfp4.hip"],
+    "k_gemm_nvfp4": ["gemm_nvfp4.hip", "gemm_fixup.hip"],
 }
+# dispatches a GEMM op may add after its main kernel (split tiles of a partial
+# last round, then their fixup); counted with the op
+SPLIT_KERNELS = ("k_gemm_nvfp4<0, true>", "k_gemm_fixup<")
 
 
 def step_dispatches():
@@ -94,7 +97,7 @@ def step_dispatches():
     for name, _, _, epi in NV_LINEARS:
         out.append(("quant_nvfp4_" + name, "k_amax_partials"))
         out.append(("quant_nvfp4_" + name, "k_quant_nvfp4"))
-        out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
+        out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d, false>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
     return out
 
 
@@ -102,7 +105,8 @@ def record_traffic(fetch_db, write_db):
     """profiles/hbm_traffic.json from the two counter runs
         rocprofv3 --pmc FETCH_SIZE --kernel-trace ... -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration
         rocprofv3 --pmc WRITE_SIZE --kernel-trace ... (same)
-    The step's dispatches are the ones right after the 1 GiB calibration copy; each
+    The step's dispatches are the ones right after the 1 GiB calibration copy (a
+    GEMM's split and fixup dispatches, when there are any, counted with it); each
     counter is scaled by what it reads for that copy (1 GiB read, 1 GiB written)."""
     import sqlite3
 
@@ -125,10 +129,18 @@ def record_traffic(fetch_db, write_db):
         i = max(copies, key=lambda j: rows[j][2])
         scale[counter] = round((1 << 20) / rows[i][2], 3)       # KiB of a 1 GiB transfer / counted KiB
         expect = step_dispatches()
-        got = rows[i + 1:i + 1 + len(expect)]
-        if [n for _, n, _ in got] != [k for _, k in expect]:
-            raise SystemExit("%s: dispatches after the copy are %s" % (counter, [n for _, n, _ in got]))
-        step[counter] = [kib for _, _, kib in got]
+        vals, j = [], i + 1
+        for _, kernel in expect:
+            if j >= len(rows) or rows[j][1] != kernel:
+                raise SystemExit("%s: expected %s at dispatch %d, found %s" % (
+                    counter, kernel, j, rows[j][1] if j < len(rows) else None))
+            kib = rows[j][2]
+            j += 1
+            while j < len(rows) and rows[j][1].startswith(SPLIT_KERNELS):
+                kib += rows[j][2]
+                j += 1
+            vals.append(kib)
+        step[counter] = vals
     rec = {}
     for idx, (op, kernel) in enumerate(step_dispatches()):
         base = kernel.split("<")[0]
@@ -212,7 +224,7 @@ class Workload:
         if name.startswith("gemm_mxfp8"):
             return "k_gemm_mxfp8<0, 0, %d>" % e
         if name.startswith("gemm_nvfp4"):
-            return "k_gemm_nvfp4<%d>" % e
+            return "k_gemm_nvfp4<%d, false>" % e
         if name.startswith("quant_mxfp8"):
             return "k_quant_mxfp8<0>"
         return "k_amax_partials + k_quant_nvfp4"
