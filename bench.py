@@ -177,6 +177,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="time the step as individual launches instead of one captured HIP graph")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     p.add_argument("--cpu-rows", type=int, default=1536, help="rows per linear in the CPU-baseline sample")
@@ -244,6 +246,15 @@ class Workload:
             out.append(("gemm_nvfp4_" + L["name"], "gemm_nv",
                         lambda L=L: mxq.gemm_nvfp4(L["aq"], L["as_"], L["ag"], L["wq"], L["ws"], L["wg"],
                                                    out=L["c"], workspace=L["gws"])))
+        return out
+
+    def outputs(self):
+        """Every tensor one step writes (codes, scales, GEMM outputs)."""
+        out = []
+        for L in self.mx:
+            out += [L["aq"], L["as_"], L["c"]]
+        for L in self.nv:
+            out += [L["aq"], L["as_"], L["ag"], L["c"]]
         return out
 
     def work(self):
@@ -468,7 +479,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = step_start.elapsed_time(step_end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = ms_per_step_eager = total_ms / args.steps
+
+    # The step as one HIP graph (captured once, replayed per step): the same
+    # launches without the host's launch gaps.  Every replay's outputs must equal
+    # the eager step's bit for bit (checked after the first replay and after the
+    # timed ones).
+    graph_check = None
+    if not args.eager:
+        outs = wl.outputs()
+        ref = [t.clone() for t in outs]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, _, f in ops:
+                f()
+        for t in outs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        first_ok = all(torch.equal(a, b) for a, b in zip(outs, ref))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step_start.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        step_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = step_start.elapsed_time(step_end) / args.steps
+        last_ok = all(torch.equal(a, b) for a, b in zip(outs, ref))
+        graph_check = {"first_replay_equals_eager": first_ok, "last_replay_equals_eager": last_ok}
+        if not (first_ok and last_ok):
+            raise SystemExit("bench.py: graph replay differs from the eager step")
 
     per_op = {}
     for i, (name, kind, _) in enumerate(ops):
@@ -551,6 +593,9 @@ def main():
         "quantizer_GB/s": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
         "quantizer_frac_of_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "wall_s": round(wall, 3),
+        "timing": "one HIP graph per step" if graph_check else "individual launches",
+        "ms_per_step_eager": round(ms_per_step_eager, 4),
+        "graph_check": graph_check,
         "ops": per_op,
         "roofline": roofline,
     }
