@@ -85,6 +85,18 @@ namespace dev {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Streaming accesses for data touched once (global_load / global_store with the
+// nt bit set): a 16-byte load and 8- and 4-byte stores.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)p));
+}
+__device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, v), (u32x2_t*)p);
+}
+__device__ __forceinline__ void store_nt(uint32_t v, uint32_t* p) { __builtin_nontemporal_store(v, p); }
+
 // Max of the 15-bit magnitudes of the eight bf16 values in a uint4, as a
 // packed pair (the caller folds the halves).  Integer order of bf16 magnitude
 // bits is the order of the magnitudes for finite values.

@@ -9,7 +9,8 @@
 //   q = RNE_sat(x / 2^E), sign bit copied from x.
 //
 // HBM-bound, one pass.  The tensor is treated as a flat stream (cols % 32 == 0,
-// so blocks never straddle rows and the scale of element e is scales[e / 32]).
+// so blocks never straddle rows and the scale of element e is scales[e / 32]),
+// read and written with streaming (nt) accesses: each byte is touched once.
 // Each lane takes 8 consecutive values (one 16-byte load), four neighbouring
 // lanes form a 32-block and find its amax with two cross-lane max steps.
 // x / 2^E is exact in fp32 (2^-E is a normal fp32 for every reachable E), and
@@ -23,7 +24,7 @@ namespace mxq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // 16-byte chunks per lane, kept in flight together
+constexpr int kUnroll = 2;  // 16-byte chunks per lane, kept in flight together
 
 template <int KIND>
 struct Fp8Traits;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     int64_t c = base + u * kThreads + t;
-    v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+    v[u] = c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
     out.x = (uint32_t)encode4<KIND>(v[u].x, v[u].y, inv);
     out.y = (uint32_t)encode4<KIND>(v[u].z, v[u].w, inv);
     if (c < n_chunks) {
-      q[c] = out;
+      dev::store_nt(out, q + c);
       if ((t & 3) == 0) s[c >> 2] = (uint8_t)(E + 127);
     }
   }

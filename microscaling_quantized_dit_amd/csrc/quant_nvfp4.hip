@@ -11,6 +11,9 @@
 //
 // Dynamic mode is two passes: k_amax_partials writes one maximum per workgroup
 // (no zero-initialised state, no atomics), k_quant_nvfp4 folds those and encodes.
+// The amax pass reads with ordinary loads, so that what it leaves in the
+// last-level cache serves the encode pass (which takes the slabs last to first);
+// the encode pass itself reads and writes with streaming (nt) accesses.
 //
 // Exact rounding at HBM speed.  Both quotients above are inexact in fp32, so
 // each is evaluated twice, with the divisor's reciprocal nudged down and up by
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     int64_t c = base + u * kThreads + t;
-    v[u] = c < n_chunks ? x[c] : make_uint4(0, 0, 0, 0);
+    v[u] = c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
   }
 
   // ---- the global decode scale s_g
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
     if (__builtin_expect(slow, 0)) codes = exact_chunk(v[u], S, sg);
     else if (__builtin_expect(S != 0.0f && codes != hi, 0)) codes = resolve_chunk(v[u], codes, hi, S, sg);
     if (c < n_chunks) {
-      q[c] = codes;
+      dev::store_nt(codes, q + c);
       if ((t & 1) == 0) s[c >> 1] = (uint8_t)sb;
     }
   }
