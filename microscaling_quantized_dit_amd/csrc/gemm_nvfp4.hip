@@ -198,11 +198,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   // read while the previous stage's group 1 runs, group 1's while the stage's own
   // group 0 runs: each when its registers are free.  Lane group g uses blocks
   // 2g, 2g + 1 of each group: the g-th 16-bit half.
-  auto read_scales = [&](v2h (&sw)[4], v2h (&sa)[4], const uint32_t* sc, int G) {
+  uint32_t dsw[4], dsa[4];                  // scale dwords on their way from LDS
+  auto read_scales = [&](const uint32_t* sc, int G) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sw[i] = scale_pair(sc[G * kTile + wrow + 32 * i] >> (16 * g));
-      sa[i] = scale_pair(sc[(2 + G) * kTile + arow + 32 * i] >> (16 * g));
+      dsw[i] = sc[G * kTile + wrow + 32 * i];
+      dsa[i] = sc[(2 + G) * kTile + arow + 32 * i];
+    }
+  };
+  auto convert_scales = [&](v2h (&sw)[4], v2h (&sa)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sw[i] = scale_pair(dsw[i] >> (16 * g));
+      sa[i] = scale_pair(dsa[i] >> (16 * g));
     }
   };
   auto read_codes = [&](uint4 (&cw)[4], uint4 (&ca)[4], const uint8_t* buf, int G) {
@@ -269,18 +277,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   // On entry dw/da[0] hold group 0's first step, dequantized.
   auto stage = [&](auto first_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
                    int dm0, int dn0, int dk0, bool dvalid) {
-    // ---- A
+    // ---- A  (group 1's scale dwords are read one K-step before they are converted,
+    // so that no wait for LDS reads stalls the MFMAs)
     read_codes(c1w, c1a, cur, 1);
-    read_scales(s1w, s1a, scur, 1);
     mfma_step(acc, I0());
     dequant(I1(), I1(), c0w, c0a, s0w, s0a);
     interleave(16, false);
     mfma_step(acc, I1());
     dequant(I0(), I2(), c0w, c0a, s0w, s0a);
     interleave(0, false);
+    read_scales(scur, 1);
     mfma_step(acc, I0());
     dequant(I1(), I3(), c0w, c0a, s0w, s0a);
-    interleave(0, false);
+    interleave(8, false);
+    convert_scales(s1w, s1a);
     mfma_step(acc, I1());
     dequant(I0(), I0(), c1w, c1a, s1w, s1a);
     interleave(0, false);
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     else __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
     dev::lds_barrier();
     // ---- C
-    read_scales(s0w, s0a, snxt, 0);
+    read_scales(snxt, 0);
     read_codes(c0w, c0a, nxt, 0);
     dma_part(0, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I0());
@@ -303,6 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     mfma_step(acc, I0());
     dequant(I1(), I3(), c1w, c1a, s1w, s1a);
     interleave(0, true);
+    convert_scales(s0w, s0a);
     dma_part(3, cur, scur, dm0, dn0, dk0, dvalid);
     mfma_step(acc, I1());
     dequant(I0(), I0(), c0w, c0a, s0w, s0a);
@@ -322,8 +333,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   }
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
   dev::lds_barrier();
-  read_scales(s0w, s0a, sc0, 0);
+  read_scales(sc0, 0);
   read_codes(c0w, c0a, lds0, 0);
+  convert_scales(s0w, s0a);
   dequant(I0(), I0(), c0w, c0a, s0w, s0a);
 
   // Global stage s uses buffer s & 1; with an even number of stages per tile every
