@@ -11,9 +11,10 @@
 //
 // Dynamic mode is two passes: k_amax_partials writes one maximum per workgroup
 // (no zero-initialised state, no atomics), k_quant_nvfp4 folds those and encodes.
-// The amax pass reads with ordinary loads, so that what it leaves in the
-// last-level cache serves the encode pass (which takes the slabs last to first);
-// the encode pass itself reads and writes with streaming (nt) accesses.
+// The amax pass reads a tensor of up to 256 MB with ordinary loads, so that what
+// it leaves in the last-level cache serves the encode pass (which takes the slabs
+// last to first), and a larger one with streaming (nt) loads; the encode pass
+// reads and writes with streaming accesses.
 //
 // Exact rounding at HBM speed.  Both quotients above are inexact in fp32, so
 // each is evaluated twice, with the divisor's reciprocal nudged down and up by
@@ -49,7 +50,10 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
   return m;
 }
 
-// Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).
+// Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).  NT:
+// streaming loads, for a tensor that a second pass will not find in the
+// last-level cache anyway (or that has no second pass).
+template <bool NT>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __restrict__ x, int64_t n_chunks,
                                                                 uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[kAmaxThreads / 64];
@@ -57,7 +61,18 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __r
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
   int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   for (; c + 3 * stride < n_chunks; c += 4 * stride) {
-    uint4 a = x[c], b = x[c + stride], d = x[c + 2 * stride], e = x[c + 3 * stride];
+    uint4 a, b, d, e;
+    if constexpr (NT) {
+      a = dev::load_nt(x + c);
+      b = dev::load_nt(x + c + stride);
+      d = dev::load_nt(x + c + 2 * stride);
+      e = dev::load_nt(x + c + 3 * stride);
+    } else {
+      a = x[c];
+      b = x[c + stride];
+      d = x[c + 2 * stride];
+      e = x[c + 3 * stride];
+    }
     pk = max_pk_u16(pk, max_pk_u16(max_pk_u16(dev::mag_max_pk(a), dev::mag_max_pk(b)),
                                    max_pk_u16(dev::mag_max_pk(d), dev::mag_max_pk(e))));
   }
@@ -415,15 +430,28 @@ __global__ __launch_bounds__(kThreads) void k_calib_fold(const uint32_t* __restr
 
 }  // namespace
 
+// The amax pass over n_chunks 16-byte chunks into n_partials partial maxima.
+// `again`: a second pass will read x right after; then ordinary loads leave it in
+// the 256 MB last-level cache, unless it is larger than that.
+static hipError_t amax_pass(const void* x, int64_t n_chunks, uint32_t* partials, int n_partials, bool again,
+                            hipStream_t stream) {
+  const bool nt = !again || n_chunks * 16 > ((int64_t)256 << 20);
+  if (nt)
+    hipLaunchKernelGGL(k_amax_partials<true>, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x,
+                       n_chunks, partials);
+  else
+    hipLaunchKernelGGL(k_amax_partials<false>, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x,
+                       n_chunks, partials);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const float* scale_in, void* q,
                                      float* scale_out, uint32_t* partials, hipStream_t stream) {
   const int64_t n_chunks = n_elems / 8;
   int n_partials = 0;
   if (!scale_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x, n_chunks,
-                       partials);
-    hipError_t e = hipGetLastError();
+    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, true, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t per_wg = (int64_t)kThreads * kUnroll;
@@ -440,9 +468,7 @@ hipError_t launch_quantize_fp8_vt(const void* v, int64_t heads, int64_t L, const
   int n_partials = 0;
   if (!scale_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)v,
-                       n_elems / 8, partials);
-    hipError_t e = hipGetLastError();
+    hipError_t e = amax_pass(v, n_elems / 8, partials, n_partials, true, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_quant_fp8_vt, dim3((unsigned)(L / 64), (unsigned)heads), dim3(kThreads), 0, stream,
@@ -454,9 +480,7 @@ hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running
                                   hipStream_t stream) {
   const int64_t n_chunks = n_elems / 8;
   const int n_partials = nvfp4_amax_partials(n_elems);
-  hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x, n_chunks,
-                     partials);
-  hipError_t e = hipGetLastError();
+  hipError_t e = amax_pass(x, n_chunks, partials, n_partials, false, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_calib_fold, dim3(1), dim3(kThreads), 0, stream, partials, n_partials, running);
   return hipGetLastError();
@@ -477,9 +501,7 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
   int n_partials = 0;
   if (!global_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream,
-                       (const uint4*)x, n_chunks, partials);
-    hipError_t e = hipGetLastError();
+    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, true, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t per_wg = (int64_t)kThreads * kUnroll;
