@@ -92,11 +92,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const float* __restrict__ ag,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const float* __restrict__ wg,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N, int K, GemmSplit sp) {
-  // two stage buffers (codes; scale dwords [W d0, W d1, A d0, A d1][row]) as distinct objects
+  // two stage buffers as distinct objects: codes, and 16 scale bytes per row
+  // ([W rows, A rows][row][4 dwords]: the stage's d0, d1, then the next stage's)
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
-  __shared__ __attribute__((aligned(16))) uint32_t sc0[4 * kTile];
-  __shared__ __attribute__((aligned(16))) uint32_t sc1[4 * kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t sc0[8 * kTile];
+  __shared__ __attribute__((aligned(16))) uint32_t sc1[8 * kTile];
   // per wave: the bias of its 128 columns (the first 256 B of one 1 KiB DMA)
   __shared__ __attribute__((aligned(16))) uint8_t bias_lds[4 * 1024];
   // per wave: output rows on their way to global memory
@@ -142,13 +143,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   // Global -> LDS: one buffer_load ... lds moves 1 KiB per wave = 16 rows of 64 B
   // (lane i -> row i / 4, physical chunk i % 4, i.e. global chunk (i % 4) ^ swz).
   // Rows 16j + i/4 have swz = (i >> 4) & 3 whatever j, so one lane offset serves
-  // all four loads of a wave's 64 rows.  Scale dwords: lane i -> row 64w + i.
+  // all four loads of a wave's 64 rows.  Scales: lane i -> row 64w + i, 16 bytes
+  // from the stage's first block on (the stage's 8 bytes and the next stage's,
+  // which are not used: one 16-byte load per row costs the texture unit half of
+  // what two 4-byte loads do; past the end of the operand the load returns zeros).
   int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   int vsc = lane * KS;
   // Every load stays inside its operand: a wave's 64 rows lie wholly inside or past
   // M (N); rows past the end, and stages after the last tile, read rows [0, 64).
   // Part p (0..3) of a stage's DMA: code rows 16p..16p+15 of this wave's 64 for W
-  // and A, and one of the four scale loads (W d0, A d0, W d1, A d1).  The parts
+  // and A, and in parts 0 and 1 the W and the A scale load.  The parts
   // are issued a quarter of a phase apart so that the four waves' loads reach the
   // texture unit spread out rather than in one burst.
   auto dma_part = [&](int p, uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
@@ -161,13 +165,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
                                              off_w + p * 16 * KP, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + p * 16 * kRowB), 16, voff,
                                              off_a + p * 16 * KP, 0, 0);
-    const int d = p >> 1;
-    if (p & 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + (2 + d) * kTile + wave * 64), 4, vsc,
-                                               off_sa + 4 * d, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + d * kTile + wave * 64), 4, vsc,
-                                               off_sw + 4 * d, 0, 0);
+    if (p == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + 4 * (wave * 64)), 16, vsc, off_sw, 0, 0);
+    else if (p == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + 4 * (kTile + wave * 64)), 16, vsc, off_sa, 0, 0);
   };
   auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
 #pragma unroll
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   auto read_scales = [&](const uint32_t* sc, int G) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dsw[i] = sc[G * kTile + wrow + 32 * i];
-      dsa[i] = sc[(2 + G) * kTile + arow + 32 * i];
+      dsw[i] = sc[4 * (wrow + 32 * i) + G];
+      dsa[i] = sc[4 * (kTile + arow + 32 * i) + G];
     }
   };
   auto convert_scales = [&](v2h (&sw)[4], v2h (&sa)[4]) {
