@@ -94,10 +94,8 @@ def step_dispatches():
     for name, _, _, epi in MX_LINEARS:
         out.append(("quant_mxfp8_" + name, "k_quant_mxfp8<0>"))
         out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
-    for name, _, K, epi in NV_LINEARS:
-        # the amax pass streams (nt loads) a tensor larger than the 256 MB last-level cache
-        big = M_NV * K * 2 > (256 << 20)
-        out.append(("quant_nvfp4_" + name, "k_amax_partials<%s>" % ("true" if big else "false")))
+    for name, _, _, epi in NV_LINEARS:
+        out.append(("quant_nvfp4_" + name, "k_amax_partials"))
         out.append(("quant_nvfp4_" + name, "k_quant_nvfp4"))
         out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d, false>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
     return out

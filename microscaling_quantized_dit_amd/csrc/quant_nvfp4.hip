@@ -11,10 +11,11 @@
 //
 // Dynamic mode is two passes: k_amax_partials writes one maximum per workgroup
 // (no zero-initialised state, no atomics), k_quant_nvfp4 folds those and encodes.
-// The amax pass reads a tensor of up to 256 MB with ordinary loads, so that what
-// it leaves in the last-level cache serves the encode pass (which takes the slabs
-// last to first), and a larger one with streaming (nt) loads; the encode pass
-// reads and writes with streaming accesses.
+// Both passes read with streaming (nt) loads and the encode pass stores the same
+// way.  (Ordinary loads in the amax pass, leaving a tensor of up to 256 MB in the
+// last-level cache for the encode pass, measured faster in isolation but 10 us
+// slower at 113 MB right after the step's GEMMs.)  The encode pass still takes
+// the slabs last to first.
 //
 // Exact rounding at HBM speed.  Both quotients above are inexact in fp32, so
 // each is evaluated twice, with the divisor's reciprocal nudged down and up by
@@ -50,10 +51,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
   return m;
 }
 
-// Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).  NT:
-// streaming loads, for a tensor that a second pass will not find in the
-// last-level cache anyway (or that has no second pass).
-template <bool NT>
+// Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __restrict__ x, int64_t n_chunks,
                                                                 uint32_t* __restrict__ partials) {
   __shared__ uint32_t red[kAmaxThreads / 64];
@@ -61,22 +59,12 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __r
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
   int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   for (; c + 3 * stride < n_chunks; c += 4 * stride) {
-    uint4 a, b, d, e;
-    if constexpr (NT) {
-      a = dev::load_nt(x + c);
-      b = dev::load_nt(x + c + stride);
-      d = dev::load_nt(x + c + 2 * stride);
-      e = dev::load_nt(x + c + 3 * stride);
-    } else {
-      a = x[c];
-      b = x[c + stride];
-      d = x[c + 2 * stride];
-      e = x[c + 3 * stride];
-    }
+    const uint4 a = dev::load_nt(x + c), b = dev::load_nt(x + c + stride);
+    const uint4 d = dev::load_nt(x + c + 2 * stride), e = dev::load_nt(x + c + 3 * stride);
     pk = max_pk_u16(pk, max_pk_u16(max_pk_u16(dev::mag_max_pk(a), dev::mag_max_pk(b)),
                                    max_pk_u16(dev::mag_max_pk(d), dev::mag_max_pk(e))));
   }
-  for (; c < n_chunks; c += stride) pk = max_pk_u16(pk, dev::mag_max_pk(x[c]));
+  for (; c < n_chunks; c += stride) pk = max_pk_u16(pk, dev::mag_max_pk(dev::load_nt(x + c)));
   uint32_t m = wave_max(dev::fold_halves_max(pk));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -192,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   __shared__ uint32_t red[kThreads / 64];
   const int t = threadIdx.x;
   // with `reverse` workgroups take the slabs last to first: right after the amax
-  // pass, the tail of x that is still in the last-level cache is read first
+  // pass, what it read last is the likeliest to be left in a cache
   const int64_t slab = reverse ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
   const int64_t base = slab * (kThreads * kUnroll);
   uint4 v[kUnroll];
@@ -431,17 +419,10 @@ __global__ __launch_bounds__(kThreads) void k_calib_fold(const uint32_t* __restr
 }  // namespace
 
 // The amax pass over n_chunks 16-byte chunks into n_partials partial maxima.
-// `again`: a second pass will read x right after; then ordinary loads leave it in
-// the 256 MB last-level cache, unless it is larger than that.
-static hipError_t amax_pass(const void* x, int64_t n_chunks, uint32_t* partials, int n_partials, bool again,
+static hipError_t amax_pass(const void* x, int64_t n_chunks, uint32_t* partials, int n_partials,
                             hipStream_t stream) {
-  const bool nt = !again || n_chunks * 16 > ((int64_t)256 << 20);
-  if (nt)
-    hipLaunchKernelGGL(k_amax_partials<true>, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x,
-                       n_chunks, partials);
-  else
-    hipLaunchKernelGGL(k_amax_partials<false>, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x,
-                       n_chunks, partials);
+  hipLaunchKernelGGL(k_amax_partials, dim3(n_partials), dim3(kAmaxThreads), 0, stream, (const uint4*)x, n_chunks,
+                     partials);
   return hipGetLastError();
 }
 
@@ -451,7 +432,7 @@ hipError_t launch_quantize_fp8_tensor(const void* x, int64_t n_elems, const floa
   int n_partials = 0;
   if (!scale_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, true, stream);
+    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t per_wg = (int64_t)kThreads * kUnroll;
@@ -468,7 +449,7 @@ hipError_t launch_quantize_fp8_vt(const void* v, int64_t heads, int64_t L, const
   int n_partials = 0;
   if (!scale_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipError_t e = amax_pass(v, n_elems / 8, partials, n_partials, true, stream);
+    hipError_t e = amax_pass(v, n_elems / 8, partials, n_partials, stream);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_quant_fp8_vt, dim3((unsigned)(L / 64), (unsigned)heads), dim3(kThreads), 0, stream,
@@ -480,7 +461,7 @@ hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running
                                   hipStream_t stream) {
   const int64_t n_chunks = n_elems / 8;
   const int n_partials = nvfp4_amax_partials(n_elems);
-  hipError_t e = amax_pass(x, n_chunks, partials, n_partials, false, stream);
+  hipError_t e = amax_pass(x, n_chunks, partials, n_partials, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_calib_fold, dim3(1), dim3(kThreads), 0, stream, partials, n_partials, running);
   return hipGetLastError();
@@ -501,7 +482,7 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
   int n_partials = 0;
   if (!global_in) {
     n_partials = nvfp4_amax_partials(n_elems);
-    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, true, stream);
+    hipError_t e = amax_pass(x, n_chunks, partials, n_partials, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t per_wg = (int64_t)kThreads * kUnroll;
