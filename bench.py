@@ -82,10 +82,11 @@ KERNEL_SOURCES = {  # HIP kernel -> sources whose text decides its code
     "k_quant_nvfp4": ["quant_nvfp4.hip"],
     "k_gemm_mxfp8": ["gemm_mxfp8.hip"],
     "k_gemm_nvfp4": ["gemm_nvfp4.hip", "gemm_fixup.hip"],
+    "k_tile_scales": ["gemm_nvfp4.hip"],
 }
 # dispatches a GEMM op may add after its main kernel (split tiles of a partial
 # last round, then their fixup); counted with the op
-SPLIT_KERNELS = ("k_gemm_nvfp4<0, true>", "k_gemm_fixup<")
+SPLIT_KERNELS = ("k_gemm_nvfp4<0, true,", "k_gemm_fixup<")
 
 
 def step_dispatches():
@@ -97,7 +98,9 @@ def step_dispatches():
     for name, _, _, epi in NV_LINEARS:
         out.append(("quant_nvfp4_" + name, "k_amax_partials"))
         out.append(("quant_nvfp4_" + name, "k_quant_nvfp4"))
-        out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d, false>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
+        # the GEMM re-lays A's and W's block scales into its own layout first
+        out.append(("gemm_nvfp4_%s (scales)" % name, "k_tile_scales<true>"))
+        out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d, false, true>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
     return out
 
 
@@ -226,7 +229,7 @@ class Workload:
         if name.startswith("gemm_mxfp8"):
             return "k_gemm_mxfp8<0, 0, %d>" % e
         if name.startswith("gemm_nvfp4"):
-            return "k_gemm_nvfp4<%d, false>" % e
+            return "k_gemm_nvfp4<%d, false, true>" % e
         if name.startswith("quant_mxfp8"):
             return "k_quant_mxfp8<0>"
         return "k_amax_partials + k_quant_nvfp4"

@@ -234,10 +234,12 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
 
 /*
  * Bytes of device workspace mxq_gemm_nvfp4 can use for this shape on the current
- * device; 0 when it has no use for one (or the shape is invalid).  With it, the
- * output tiles that would otherwise run in a partial last round on the compute
- * units are cut along K into ranges computed side by side, and their fp32 partial
- * sums are added by a second kernel before the epilogue.
+ * device (0 for an invalid shape).  With it, both operands' block scales are first
+ * rewritten into the GEMM's own layout (64-row blocks, one 512-byte run per 128-K
+ * stage, so that a stage's scales arrive as one contiguous load), and the output
+ * tiles that would otherwise run in a partial last round on the compute units
+ * are cut along K into ranges computed side by side, whose fp32 partial sums are
+ * added by a second kernel before the epilogue.  Its contents are scratch.
  */
 size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K);
 
@@ -248,10 +250,11 @@ size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K);
  *   a_q, a_scales, a_global : packed E2M1 [M, K/2], E4M3 [M, K/16], device fp32 s_ga.
  *   w_q, w_scales, w_global : packed E2M1 [N, K/2], E4M3 [N, K/16], device fp32 s_gw.
  *   M, N, K, bias, epi, c   : as mxq_gemm_mxfp8.
- *   workspace, ws_bytes     : NULL (no split), or device scratch of at least
- *                             mxq_gemm_nvfp4_workspace_size(M, N, K) bytes, 16-byte
- *                             aligned (else MXQ_ERROR_WORKSPACE / MXQ_ERROR_MISALIGNED);
- *                             calls sharing one must be ordered on one stream.
+ *   workspace, ws_bytes     : NULL (scales read in place, no split), or device
+ *                             scratch of at least mxq_gemm_nvfp4_workspace_size(M, N, K)
+ *                             bytes, 16-byte aligned (else MXQ_ERROR_WORKSPACE /
+ *                             MXQ_ERROR_MISALIGNED); calls sharing one must be
+ *                             ordered on one stream.
  *   The fp32 additions of a split tile's parts come in a different order than an
  *   unsplit accumulation; results agree within the GEMM tolerance, not bit for bit.
  */

@@ -27,9 +27,17 @@
 // in NVFP4 block 2g + j/2 of the group, so each lane's step has a single scale.
 //
 // Tiling as the MXFP8 kernel: 256 x 256 output tiles, 4 waves of 128 x 128,
-// codes and scale dwords copied global -> LDS by buffer_load ... lds into two
+// codes and block scales copied global -> LDS by buffer_load ... lds into two
 // stage buffers of 128 K (64-byte rows, XOR-swizzled), one 64-K group per half
 // stage with the mid-stage barrier between them; persistent over tiles.
+//
+// Scale layout.  The texture unit's work for a load goes by the rows (cache
+// lines) it touches, and a stage needs only 8 scale bytes of each of 64 rows per
+// wave and operand.  Given a workspace, k_tile_scales first rewrites both
+// operands' scales into 64-row blocks, stage by stage ([R/64][K/128][64][8 B]),
+// and the GEMM (TILED) then fetches a stage's scales for its 64 rows as one
+// contiguous 1 KiB load per wave and operand (with the next stage's along).
+// Without one it reads them in place, 16 bytes per row.
 #include <type_traits>
 
 #include "mxq_internal.h"
@@ -87,13 +95,15 @@ __device__ __forceinline__ uint32_t word(const uint4& v) {
 // PART = false: tiles [0, sp.dp_tiles) whole, round-robin over the workgroups.
 // PART = true: one K range of a split tile per workgroup, its fp32 sum into
 // sp.partial (the fixup kernel completes the tile).
-template <int EPI, bool PART>
+// TILED: as_ and ws are the scales rewritten by k_tile_scales.
+template <int EPI, bool PART, bool TILED>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const float* __restrict__ ag,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws, const float* __restrict__ wg,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N, int K, GemmSplit sp) {
-  // two stage buffers as distinct objects: codes, and 16 scale bytes per row
-  // ([W rows, A rows][row][4 dwords]: the stage's d0, d1, then the next stage's)
+  // two stage buffers as distinct objects: codes, and 16 scale bytes per row (in
+  // place: [W rows, A rows][row][4 dwords], the stage's d0, d1, then the next
+  // stage's; TILED: [W, A][wave][next stage?][64 rows][2 dwords])
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStage];
   __shared__ __attribute__((aligned(16))) uint32_t sc0[8 * kTile];
@@ -138,6 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, M * KP, 0x00020000);
   const auto rsw = __builtin_amdgcn_make_buffer_rsrc((void*)ws, (short)0, N * KS, 0x00020000);
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc((void*)as_, (short)0, M * KS, 0x00020000);
+  const int NST = K / kBK;          // stages per row (TILED scale blocks per 64-row block)
   const auto rb = __builtin_amdgcn_make_buffer_rsrc((void*)bias, (short)0, EPI >= 1 ? N * 2 : 0, 0x00020000);
 
   // Global -> LDS: one buffer_load ... lds moves 1 KiB per wave = 16 rows of 64 B
@@ -148,9 +159,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   // which are not used: one 16-byte load per row costs the texture unit half of
   // what two 4-byte loads do; past the end of the operand the load returns zeros).
   int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  int vsc = lane * KS;
-  // Every load stays inside its operand: a wave's 64 rows lie wholly inside or past
-  // M (N); rows past the end, and stages after the last tile, read rows [0, 64).
+  int vsc = TILED ? lane * 16 : lane * KS;
+  // Every code load stays inside its operand: a wave's 64 rows lie wholly inside
+  // or past M (N); rows past the end, and stages after the last tile, read rows
+  // [0, 64).  (A scale load can reach 8 bytes past the end, see above.)
   // Part p (0..3) of a stage's DMA: code rows 16p..16p+15 of this wave's 64 for W
   // and A, and in parts 0 and 1 the W and the A scale load.  The parts
   // are issued a quarter of a phase apart so that the four waves' loads reach the
@@ -159,16 +171,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
     const bool vw = valid && rw0 < N, va = valid && ra0 < M;
     const int off_w = vw ? rw0 * KP + k0 / 2 : 0, off_a = va ? ra0 * KP + k0 / 2 : 0;
-    const int off_sw = vw ? rw0 * KS + k0 / 16 : 0, off_sa = va ? ra0 * KS + k0 / 16 : 0;
+    const int st = k0 / kBK;
+    const int off_sw = vw ? (TILED ? ((rw0 >> 6) * NST + st) * 512 : rw0 * KS + k0 / 16) : 0;
+    const int off_sa = va ? (TILED ? ((ra0 >> 6) * NST + st) * 512 : ra0 * KS + k0 / 16) : 0;
     uint8_t* base = buf + wave * 64 * kRowB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + p * 16 * kRowB), 16, voff,
                                              off_w + p * 16 * KP, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + p * 16 * kRowB), 16, voff,
                                              off_a + p * 16 * KP, 0, 0);
+    // both layouts: 1 KiB per wave and operand at dword 256 * (4 op + w)
     if (p == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + 4 * (wave * 64)), 16, vsc, off_sw, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + 256 * wave), 16, vsc, off_sw, 0, 0);
     else if (p == 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + 4 * (kTile + wave * 64)), 16, vsc, off_sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + 256 * (4 + wave)), 16, vsc, off_sa, 0, 0);
   };
   auto dma_stage = [&](uint8_t* buf, uint32_t* sc, int m0, int n0, int k0, bool valid) {
 #pragma unroll
@@ -186,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     r = lane & 31;
     g = lane >> 5;
     voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-    vsc = lane * KS;
+    vsc = TILED ? lane * 16 : lane * KS;
     x = swz(r);
     wrow = wn * 128 + r;
     arow = wm * 128 + r;
@@ -203,8 +218,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   auto read_scales = [&](const uint32_t* sc, int G) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dsw[i] = sc[4 * (wrow + 32 * i) + G];
-      dsa[i] = sc[4 * (kTile + arow + 32 * i) + G];
+      if constexpr (TILED) {   // row R: dword 256 * (4 op + R / 64) + 2 (R % 64) + G
+        dsw[i] = sc[256 * (2 * wn + (i >> 1)) + 2 * (32 * (i & 1) + r) + G];
+        dsa[i] = sc[256 * (4 + 2 * wm + (i >> 1)) + 2 * (32 * (i & 1) + r) + G];
+      } else {
+        dsw[i] = sc[4 * (wrow + 32 * i) + G];
+        dsa[i] = sc[4 * (kTile + arow + 32 * i) + G];
+      }
     }
   };
   auto convert_scales = [&](v2h (&sw)[4], v2h (&sa)[4]) {
@@ -387,6 +407,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);   // no DMA outlives the workgroup
 }
 
+// Scales [R, K/16] row-major -> [R/64][K/128][64 rows][8 B]: a stage's 8 bytes of
+// 64 consecutive rows become 512 contiguous bytes.  One launch for both operands:
+// workgroup (x, y) takes 16 stages of 64-row block y, of A's rows for y < ra64 and
+// of W's after them.  The rows' segments go through LDS so that both the reads
+// (along a row) and the writes (along a stage block) are contiguous.  V16: rows
+// start 16-byte aligned (K a multiple of 256), so the reads are 16 bytes wide.
+template <bool V16>
+__global__ __launch_bounds__(256) void k_tile_scales(const uint8_t* __restrict__ a_src, uint8_t* __restrict__ a_dst,
+                                                     int ra64, const uint8_t* __restrict__ w_src,
+                                                     uint8_t* __restrict__ w_dst, int KS, int nst) {
+  __shared__ __attribute__((aligned(16))) uint8_t seg[64 * 128];   // [row][16 stages][8 B]
+  const int t = threadIdx.x;
+  const bool is_a = (int)blockIdx.y < ra64;
+  const int rb = is_a ? (int)blockIdx.y : (int)blockIdx.y - ra64;
+  const uint8_t* src = is_a ? a_src : w_src;
+  uint8_t* dst = is_a ? a_dst : w_dst;
+  const int st0 = blockIdx.x * 16, ns = min(16, nst - st0);
+  {  // thread t: row t / 4, stages 4 (t % 4) .. +3 of the group (32 bytes)
+    const int row = t >> 2, st = 4 * (t & 3);
+    const uint8_t* p = src + (size_t)(rb * 64 + row) * KS + (size_t)(st0 + st) * 8;
+    uint8_t* q = seg + row * 128 + st * 8;
+    if (V16) {
+      if (st < ns) *(uint4*)q = *(const uint4*)p;                       // stages st, st + 1
+      if (st + 2 < ns) *(uint4*)(q + 16) = *(const uint4*)(p + 16);     // (nst is even here)
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (st + u < ns) *(uint2*)(q + 8 * u) = *(const uint2*)(p + 8 * u);
+    }
+  }
+  __syncthreads();
+  {  // thread t: stage t / 16, rows 4 (t % 16) .. +3: 32 contiguous bytes of its block
+    const int st = t >> 4, r0 = 4 * (t & 15);
+    if (st < ns) {
+      uint2 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *(const uint2*)(seg + (r0 + q) * 128 + st * 8);
+      uint4* o = (uint4*)(dst + ((size_t)rb * nst + st0 + st) * 512 + r0 * 8);
+      o[0] = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+      o[1] = make_uint4(v[2].x, v[2].y, v[3].x, v[3].y);
+    }
+  }
+}
+
 }  // namespace
 
 static GemmSplit nvfp4_split(int64_t M, int64_t N, int64_t K) {
@@ -396,8 +460,13 @@ static GemmSplit nvfp4_split(int64_t M, int64_t N, int64_t K) {
   return plan_gemm_split(tiles, device_compute_units(), nk);
 }
 
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace: the split's partial tiles (if any), then A's and W's scales in the
+// layout k_tile_scales writes.
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return gemm_split_bytes(nvfp4_split(M, N, K), (int)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile)));
+  const size_t split = gemm_split_bytes(nvfp4_split(M, N, K), (int)(((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile)));
+  return round256(split) + round256((size_t)M * (K / 16)) + round256((size_t)N * (K / 16));
 }
 
 // Shapes reaching here are validated: M, N, K positive multiples of 128, epi 0..2;
@@ -422,20 +491,42 @@ hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g,
   auto As = (const uint8_t*)a_s;
   auto W = (const uint8_t*)w_q;
   auto Ws = (const uint8_t*)w_s;
+  // With a workspace, both operands' scales in the GEMM's layout first.
+  const bool tiled = workspace != nullptr;
+  if (tiled) {
+    const int KS = k / 16, nst = k / kBK;
+    uint8_t* at = (uint8_t*)workspace + round256(gemm_split_bytes(nvfp4_split(M, N, K), tiles));
+    uint8_t* wt = at + round256((size_t)M * KS);
+    const dim3 tg((nst + 15) / 16, m / 64 + n / 64);
+    if (KS % 16 == 0)
+      hipLaunchKernelGGL(k_tile_scales<true>, tg, dim3(256), 0, stream, As, at, m / 64, Ws, wt, KS, nst);
+    else
+      hipLaunchKernelGGL(k_tile_scales<false>, tg, dim3(256), 0, stream, As, at, m / 64, Ws, wt, KS, nst);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    As = at;
+    Ws = wt;
+  }
   auto B = (const uint16_t*)bias;
   auto C = (uint16_t*)c;
   dim3 block(kThreads);
   dim3 grid(persistent ? cus : tiles);
-  if (epi == 0)
-    hipLaunchKernelGGL((k_gemm_nvfp4<0, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
-  else if (epi == 1)
-    hipLaunchKernelGGL((k_gemm_nvfp4<1, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
-  else
-    hipLaunchKernelGGL((k_gemm_nvfp4<2, false>), grid, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+#define MXQ_NV_LAUNCH(E, P, T, G)                                                                               \
+  hipLaunchKernelGGL((k_gemm_nvfp4<E, P, T>), G, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp)
+  if (tiled) {
+    if (epi == 0) MXQ_NV_LAUNCH(0, false, true, grid);
+    else if (epi == 1) MXQ_NV_LAUNCH(1, false, true, grid);
+    else MXQ_NV_LAUNCH(2, false, true, grid);
+  } else {
+    if (epi == 0) MXQ_NV_LAUNCH(0, false, false, grid);
+    else if (epi == 1) MXQ_NV_LAUNCH(1, false, false, grid);
+    else MXQ_NV_LAUNCH(2, false, false, grid);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.parts) return e;
   dim3 grid_p((tiles - sp.dp_tiles) * sp.parts);
-  hipLaunchKernelGGL((k_gemm_nvfp4<0, true>), grid_p, block, 0, stream, A, As, a_g, W, Ws, w_g, B, C, m, n, k, sp);
+  MXQ_NV_LAUNCH(0, true, true, grid_p);   // a split implies a workspace
+#undef MXQ_NV_LAUNCH
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_fixup(sp, M, N, a_g, w_g, bias, epi, c, stream);

@@ -161,12 +161,16 @@ def test_gemm_nvfp4_validation(lib):
     assert call(ag=FAKE + 1) == MISALIGNED
     # a shape with a partial last round (17 x 16 tiles on 256 compute units, the
     # count assumed without a device) wants a workspace; too small a one is refused
+    def scales(M, N, K):                                 # both operands' scales, re-laid out
+        return M * K // 16 + N * K // 16
+
     need = lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1024)
-    assert need == 16 * 4 * 256 * 256 * 4               # 16 leftover tiles, 4 K-parts, fp32
+    assert need == 16 * 4 * 256 * 256 * 4 + scales(4352, 4096, 1024)   # 16 leftover tiles, 4 K-parts, fp32
     assert call(M=4352, N=4096, K=1024, ws=FAKE, nbytes=need - 1) == WORKSPACE
     assert call(M=4352, N=4096, K=1024, ws=FAKE + 8, nbytes=need) == MISALIGNED
-    assert lib.mxq_gemm_nvfp4_workspace_size(4096, 4096, 1024) == 0    # 256 tiles: one full round
-    assert lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1152) == 0    # odd stage count: no persistence
+    assert lib.mxq_gemm_nvfp4_workspace_size(4096, 4096, 1024) == scales(4096, 4096, 1024)   # one full round
+    assert lib.mxq_gemm_nvfp4_workspace_size(4352, 4096, 1152) == scales(4352, 4096, 1152)   # odd stages: no split
+    assert lib.mxq_gemm_nvfp4_workspace_size(128, 384, 128) == 128 * 8 + 384 * 8
     assert lib.mxq_gemm_nvfp4_workspace_size(100, 4096, 1024) == 0
 
 

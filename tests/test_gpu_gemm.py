@@ -172,6 +172,25 @@ def test_more_tiles_than_compute_units(mxq, K):
     _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias"), "nv K=%d" % K)
 
 
+@pytest.mark.parametrize("M,N,K", [(384, 640, 256), (640, 384, 1152), (4096, 4096, 1024), (128, 128, 128)])
+def test_nvfp4_scale_layouts_agree(mxq, M, N, K):
+    """Given a workspace, the NVFP4 GEMM first re-lays both operands' block scales
+    into its own layout; without one it reads them in place.  At shapes with no
+    split (fewer tiles than compute units, an odd stage count, exactly one full
+    round) both must give the same bits, and match the oracle."""
+    import torch
+    A = NV(inputs.flux_activation(M, K, seed=K, stream="layouts/A"))
+    W = NV(inputs.weight(N, K, seed=K, stream="layouts/W"))
+    b = inputs.bias(N, K, seed=K, stream="layouts/b")
+    db = inputs.to_torch(b, "cuda")
+    ws = torch.empty((mxq.gemm_nvfp4_workspace_size(M, N, K),), dtype=torch.uint8, device="cuda")
+    c1 = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, bias=db, epi="bias_gelu", workspace=ws)
+    c2 = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, bias=db, epi="bias_gelu", split=False)
+    assert torch.equal(c1, c2)
+    r = oracle.gemm_nvfp4(A.q, A.s, A.g, W.q, W.s, W.g, bias=b, epi=oracle.EPI_BIAS_GELU_TANH)
+    _assert_close(_bf16_out(c1), r, "nv layouts %dx%dx%d" % (M, N, K))
+
+
 def test_deterministic(mxq):
     import torch
     A = NV(inputs.flux_activation(512, 1024, seed=2, stream="det/A"))
