@@ -50,6 +50,10 @@ NV_LINEARS = [  # name, N, K, epilogue   (M = 18432)
     ("linear2", 3072, 15360, "none"),
 ]
 M_MX, M_NV = 4608, 18432
+# block scales travel in the GEMM-tiled order: the quantizers write it, the GEMMs
+# fetch a K step's scales for 64 rows as one contiguous load
+SCALES = "tiled"
+TILED_NAME = "true" if SCALES == "tiled" else "false"   # template argument in kernel names
 
 
 def measured_traffic(kernel):
@@ -82,7 +86,6 @@ KERNEL_SOURCES = {  # HIP kernel -> sources whose text decides its code
     "k_quant_nvfp4": ["quant_nvfp4.hip"],
     "k_gemm_mxfp8": ["gemm_mxfp8.hip"],
     "k_gemm_nvfp4": ["gemm_nvfp4.hip", "gemm_fixup.hip"],
-    "k_tile_scales": ["gemm_nvfp4.hip"],
 }
 # dispatches a GEMM op may add after its main kernel (split tiles of a partial
 # last round, then their fixup); counted with the op
@@ -93,13 +96,12 @@ def step_dispatches():
     """(op name, kernel function) of every dispatch of one step, in launch order."""
     out = []
     for name, _, _, epi in MX_LINEARS:
-        out.append(("quant_mxfp8_" + name, "k_quant_mxfp8<0>"))
-        out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
+        out.append(("quant_mxfp8_" + name, "k_quant_mxfp8<0, %s>" % TILED_NAME))
+        out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d, %s>" % ({"none": 0, "bias": 1, "bias_gelu": 2}[epi],
+                                                                           TILED_NAME)))
     for name, _, _, epi in NV_LINEARS:
         out.append(("quant_nvfp4_" + name, "k_amax_partials"))
-        out.append(("quant_nvfp4_" + name, "k_quant_nvfp4"))
-        # the GEMM re-lays A's and W's block scales into its own layout first
-        out.append(("gemm_nvfp4_%s (scales)" % name, "k_tile_scales<true>"))
+        out.append(("quant_nvfp4_" + name, "k_quant_nvfp4<%s>" % TILED_NAME))
         out.append(("gemm_nvfp4_" + name, "k_gemm_nvfp4<%d, false, true>" % {"none": 0, "bias": 1, "bias_gelu": 2}[epi]))
     return out
 
@@ -200,7 +202,7 @@ class Workload:
             x = inputs.to_torch(inputs.flux_activation(M_MX, K, seed=0, stream="bench/%s/A" % name), dev)
             w = inputs.to_torch(inputs.weight(N, K, seed=0, stream="bench/%s/W" % name), dev)
             b = inputs.to_torch(inputs.bias(N, K, seed=0, stream="bench/%s/b" % name), dev) if epi != "none" else None
-            wq, ws = mxq.quantize_mxfp8(w)
+            wq, ws = mxq.quantize_mxfp8(w, scale_layout=SCALES)
             aq = torch.empty((M_MX, K), dtype=torch.uint8, device=dev)
             as_ = torch.empty((M_MX, K // 32), dtype=torch.uint8, device=dev)
             c = torch.empty((M_MX, N), dtype=torch.bfloat16, device=dev)
@@ -209,7 +211,7 @@ class Workload:
         for name, N, K, epi in NV_LINEARS:
             x = inputs.to_torch(inputs.flux_activation(M_NV, K, seed=0, stream="bench/%s/A" % name), dev)
             w = inputs.to_torch(inputs.weight(N, K, seed=0, stream="bench/%s/W" % name), dev)
-            wq, ws, wg = mxq.quantize_nvfp4(w)
+            wq, ws, wg = mxq.quantize_nvfp4(w, scale_layout=SCALES)
             aq = torch.empty((M_NV, K // 2), dtype=torch.uint8, device=dev)
             as_ = torch.empty((M_NV, K // 16), dtype=torch.uint8, device=dev)
             ag = torch.empty((1,), dtype=torch.float32, device=dev)
@@ -227,28 +229,29 @@ class Workload:
         """HIP kernel function an op launches (the GEMM kernels are templated on the epilogue)."""
         e = {"none": 0, "bias": 1, "bias_gelu": 2}[epi]
         if name.startswith("gemm_mxfp8"):
-            return "k_gemm_mxfp8<0, 0, %d>" % e
+            return "k_gemm_mxfp8<0, 0, %d, %s>" % (e, TILED_NAME)
         if name.startswith("gemm_nvfp4"):
             return "k_gemm_nvfp4<%d, false, true>" % e
         if name.startswith("quant_mxfp8"):
-            return "k_quant_mxfp8<0>"
-        return "k_amax_partials + k_quant_nvfp4"
+            return "k_quant_mxfp8<0, %s>" % TILED_NAME
+        return "k_amax_partials + k_quant_nvfp4<%s>" % TILED_NAME
 
     def ops(self, mxq):
         """(op name, kind, callable) in step order."""
         out = []
         for L in self.mx:
             out.append(("quant_mxfp8_" + L["name"], "quant_mx",
-                        lambda L=L: mxq.quantize_mxfp8(L["x"], "e4m3", out=(L["aq"], L["as_"]))))
+                        lambda L=L: mxq.quantize_mxfp8(L["x"], "e4m3", out=(L["aq"], L["as_"]), scale_layout=SCALES)))
             out.append(("gemm_mxfp8_" + L["name"], "gemm_mx",
                         lambda L=L: mxq.gemm_mxfp8(L["aq"], L["as_"], L["wq"], L["ws"], bias=L["b"], epi=L["epi"],
-                                                   out=L["c"])))
+                                                   out=L["c"], scale_layout=SCALES)))
         for L in self.nv:
             out.append(("quant_nvfp4_" + L["name"], "quant_nv",
-                        lambda L=L: mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], L["ag"]), workspace=L["wsb"])))
+                        lambda L=L: mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], L["ag"]), workspace=L["wsb"],
+                                                       scale_layout=SCALES)))
             out.append(("gemm_nvfp4_" + L["name"], "gemm_nv",
                         lambda L=L: mxq.gemm_nvfp4(L["aq"], L["as_"], L["ag"], L["wq"], L["ws"], L["wg"],
-                                                   out=L["c"], workspace=L["gws"])))
+                                                   out=L["c"], workspace=L["gws"], scale_layout=SCALES)))
         return out
 
     def outputs(self):
@@ -293,10 +296,10 @@ def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
         g = torch.empty((1,), dtype=torch.float32, device="cuda")
 
         def run_static():
-            mxq.quantize_nvfp4(L["x"], global_scale=running, out=(L["aq"], L["as_"], g))
+            mxq.quantize_nvfp4(L["x"], global_scale=running, out=(L["aq"], L["as_"], g), scale_layout=SCALES)
 
         def run_dynamic():
-            mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], g), workspace=L["wsb"])
+            mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], g), workspace=L["wsb"], scale_layout=SCALES)
 
         res = {}
         for tag, f in (("static", run_static), ("dynamic", run_dynamic)):
@@ -590,6 +593,7 @@ def main():
             "workload": "FLUX DiT block linears: double-stream MXFP8 E4M3 at M=4608 (QKV, out-proj, "
                         "MLP-up +bias+GELU, MLP-down) + single-stream NVFP4 at M=18432 (linear1, linear2); "
                         "each activation quantized per step, weights pre-quantized",
+            "scale_layout": SCALES,
             "global_batch": 1, "seq_len": M_MX, "parallelism": "single GPU",
         },
         "gemm_TFLOP/s": round(gemm_flops / (g_ms * 1e-3) / 1e12, 1),

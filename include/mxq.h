@@ -35,7 +35,7 @@
  *     S_b = RN_E4M3_sat(amax_block / (6 s_g)) (may be 0); q = RN_E2M1_sat(x / (S_b s_g)),
  *     magnitude 0 when S_b = 0; dequantized value = val(q) * val(S_b) * s_g.
  *
- * Layouts (all row-major, no padding):
+ * Layouts (row-major, no padding; block scales also in a tiled order, below):
  *   x        bf16  [rows, cols]            cols contiguous (K for a GEMM operand)
  *   MXFP8 q  u8    [rows, cols]            E4M3 or E5M2 codes
  *   MXFP8 s  u8    [rows, cols / 32]       E8M0 scale bytes
@@ -87,16 +87,36 @@ typedef enum {
 } mxq_epilogue;
 
 /*
+ * Byte order of a block-scale array [rows, cols / B] (B = 32 for MXFP8, 16 for
+ * NVFP4); the size is rows * cols / B bytes in both.  This is a storage choice of
+ * this library, not a format of the pages.
+ *   MXQ_SCALES_ROW_MAJOR : scale (r, j) at byte r * (cols / B) + j.
+ *   MXQ_SCALES_TILED     : rows in blocks of 64, K in steps of 128 values; with
+ *                          P = 128 / B scales per row and step (4 MXFP8, 8 NVFP4)
+ *                          scale (r, j) at byte
+ *                            ((r / 64) * (cols / 128) + j / P) * 64 P + (r % 64) P + j % P,
+ *                          i.e. one contiguous run of 64 P bytes per (row block,
+ *                          K step): the GEMMs fetch a K step's scales for 64 rows
+ *                          with one contiguous load.  Needs rows % 64 == 0 and
+ *                          cols % 128 == 0.
+ * Quantizers write either order; the GEMMs read both operands' scales in the one
+ * order they are given.  Codes are row-major in both.
+ */
+typedef enum { MXQ_SCALES_ROW_MAJOR = 0, MXQ_SCALES_TILED = 1 } mxq_scale_layout;
+
+/*
  * MXFP8 quantizer [P1 "MXFP8和NVFP4技术背景解析"; P5 step 2].
  *   x      : bf16 [rows, cols], device, read only.
  *   rows   : > 0.   cols: > 0 and a multiple of 32 (else MXQ_ERROR_UNSUPPORTED_SHAPE).
  *   kind   : element format, E4M3 or E5M2.
  *   q      : u8 [rows, cols], device, written.
- *   scales : u8 [rows, cols/32] E8M0, device, written.
+ *   scales : u8 [rows, cols/32] E8M0, device, written in the order scale_layout
+ *            names (MXQ_SCALES_TILED: rows % 64 == 0 and cols % 128 == 0, else
+ *            MXQ_ERROR_UNSUPPORTED_SHAPE).
  * One pass over x; codes and scales are bit-exact to the definition above.
  */
 mxq_status mxq_quantize_mxfp8(const void* x, int64_t rows, int64_t cols, mxq_fp8_kind kind,
-                              void* q, void* scales, void* stream);
+                              void* q, void* scales, mxq_scale_layout scale_layout, void* stream);
 
 /* Bytes of device workspace mxq_quantize_nvfp4 needs (dynamic mode) for this
  * shape; 0 for invalid shapes.  The workspace holds per-workgroup partial
@@ -112,7 +132,8 @@ size_t mxq_quantize_nvfp4_workspace_size(int64_t rows, int64_t cols);
  *                      positive and finite), or NULL for the dynamic scale
  *                      s_g = RN_fp32(amax(x) / 2688) taken over the whole tensor.
  *   q                : u8 [rows, cols/2] packed E2M1, device, written.
- *   scales           : u8 [rows, cols/16] E4M3, device, written.
+ *   scales           : u8 [rows, cols/16] E4M3, device, written in the order
+ *                      scale_layout names (tiled: rows % 64 == 0, cols % 128 == 0).
  *   global_scale_out : device fp32, written with the s_g used (both modes).
  *   workspace        : device scratch of mxq_quantize_nvfp4_workspace_size bytes
  *                      (dynamic mode; may be NULL in static mode).
@@ -121,8 +142,8 @@ size_t mxq_quantize_nvfp4_workspace_size(int64_t rows, int64_t cols);
  */
 mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols,
                               const float* global_scale_in, void* q, void* scales,
-                              float* global_scale_out, void* workspace, size_t ws_bytes,
-                              void* stream);
+                              mxq_scale_layout scale_layout, float* global_scale_out,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Static-scale calibration for NVFP4 activations [P5 step 1 "校准": run a small
@@ -223,20 +244,23 @@ mxq_status mxq_gemm_bf16_fp8w(const void* a, const void* w_q, const float* w_sca
  *   a_q, a_scales : A codes u8 [M, K] and E8M0 [M, K/32] (from mxq_quantize_mxfp8).
  *   w_q, w_scales : W codes u8 [N, K] and E8M0 [N, K/32].
  *   a_kind, w_kind: element formats of A and W (E4M3 / E5M2, may differ).
+ *   scale_layout  : order of both a_scales and w_scales; the tiled order saves
+ *                   the GEMM scattered scale loads.
  *   M, N, K       : > 0, multiples of 128 (else MXQ_ERROR_UNSUPPORTED_SHAPE).
  *   bias          : bf16 [N] device (required unless epi == MXQ_EPI_NONE).
  *   c             : bf16 [M, N] device, written.
  */
 mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_kind,
                           const void* w_q, const void* w_scales, mxq_fp8_kind w_kind,
+                          mxq_scale_layout scale_layout,
                           int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi,
                           void* c, void* stream);
 
 /*
  * Bytes of device workspace mxq_gemm_nvfp4 can use for this shape on the current
- * device (0 for an invalid shape).  With it, both operands' block scales are first
- * rewritten into the GEMM's own layout (64-row blocks, one 512-byte run per 128-K
- * stage, so that a stage's scales arrive as one contiguous load), and the output
+ * device (0 for an invalid shape).  With it, row-major block scales of both
+ * operands are first rewritten into the tiled order (MXQ_SCALES_TILED; scales
+ * given tiled are read in place and that part goes unused), and the output
  * tiles that would otherwise run in a partial last round on the compute units
  * are cut along K into ranges computed side by side, whose fp32 partial sums are
  * added by a second kernel before the epilogue.  Its contents are scratch.
@@ -249,6 +273,7 @@ size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K);
  *                  (+ bias[n]) ), fp32 accumulation, one RNE to bf16.
  *   a_q, a_scales, a_global : packed E2M1 [M, K/2], E4M3 [M, K/16], device fp32 s_ga.
  *   w_q, w_scales, w_global : packed E2M1 [N, K/2], E4M3 [N, K/16], device fp32 s_gw.
+ *   scale_layout            : order of both a_scales and w_scales.
  *   M, N, K, bias, epi, c   : as mxq_gemm_mxfp8.
  *   workspace, ws_bytes     : NULL (scales read in place, no split), or device
  *                             scratch of at least mxq_gemm_nvfp4_workspace_size(M, N, K)
@@ -260,6 +285,7 @@ size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K);
  */
 mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_global,
                           const void* w_q, const void* w_scales, const float* w_global,
+                          mxq_scale_layout scale_layout,
                           int64_t M, int64_t N, int64_t K, const void* bias, mxq_epilogue epi,
                           void* c, void* workspace, size_t ws_bytes, void* stream);
 

@@ -27,6 +27,7 @@ E4M3, E5M2 = 0, 1
 EPI_NONE, EPI_BIAS, EPI_BIAS_GELU_TANH = 0, 1, 2
 _EPI = {"none": 0, "bias": 1, "bias_gelu": 2, "bias_gelu_tanh": 2, 0: 0, 1: 1, 2: 2, None: 0}
 _KIND = {"e4m3": 0, "e5m2": 1, 0: 0, 1: 1}
+_LAYOUT = {"row": 0, "tiled": 1, 0: 0, 1: 1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxq.so")
@@ -62,17 +63,17 @@ def load():
         import torch  # noqa: F401
         lib = ctypes.CDLL(_LIB_PATH)
         P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
-        lib.mxq_quantize_mxfp8.argtypes = [P, i64, i64, i32, P, P, P]
+        lib.mxq_quantize_mxfp8.argtypes = [P, i64, i64, i32, P, P, i32, P]
         lib.mxq_quantize_nvfp4_workspace_size.argtypes = [i64, i64]
         lib.mxq_quantize_nvfp4_workspace_size.restype = sz
-        lib.mxq_quantize_nvfp4.argtypes = [P, i64, i64, P, P, P, P, P, sz, P]
+        lib.mxq_quantize_nvfp4.argtypes = [P, i64, i64, P, P, P, i32, P, P, sz, P]
         lib.mxq_nvfp4_calibrate.argtypes = [P, i64, i64, P, P, sz, P]
         lib.mxq_quantize_fp8_weight.argtypes = [P, i64, i64, P, P, P, P, sz, P]
         lib.mxq_gemm_bf16_fp8w.argtypes = [P, P, P, i64, i64, i64, P, i32, P, P]
-        lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i64, i64, i64, P, i32, P, P]
+        lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i32, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_nvfp4_workspace_size.argtypes = [i64, i64, i64]
         lib.mxq_gemm_nvfp4_workspace_size.restype = sz
-        lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, i32, P, P, sz, P]
+        lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i32, i64, i64, i64, P, i32, P, P, sz, P]
         lib.mxq_quantize_fp8_v.argtypes = [P, i64, i64, i64, P, P, P, P, sz, P]
         lib.mxq_attention_fp8.argtypes = [P, P, P, P, P, P, i64, i64, i64, P, P]
         lib.mxq_status_string.argtypes = [i32]
@@ -125,8 +126,10 @@ def _need(t, dtype, name, device=None):
 
 # ------------------------------------------------------------------ quantizers
 
-def quantize_mxfp8(x, kind="e4m3", out=None, stream=None):
-    """bf16 [R, C] -> (codes uint8 [R, C], E8M0 scales uint8 [R, C/32])."""
+def quantize_mxfp8(x, kind="e4m3", out=None, stream=None, scale_layout="row"):
+    """bf16 [R, C] -> (codes uint8 [R, C], E8M0 scales uint8 [R, C/32]).  The
+    scales' bytes are in row-major order ("row") or in the GEMM-tiled order
+    ("tiled", R % 64 == 0 and C % 128 == 0; the tensor keeps the shape [R, C/32])."""
     torch = _torch()
     _need(x, torch.bfloat16, "x")
     if x.dim() != 2:
@@ -136,7 +139,8 @@ def quantize_mxfp8(x, kind="e4m3", out=None, stream=None):
         torch.empty((R, C), dtype=torch.uint8, device=x.device),
         torch.empty((R, C // 32), dtype=torch.uint8, device=x.device))
     lib = load()
-    _check(lib.mxq_quantize_mxfp8(_ptr(x), R, C, _KIND[kind], _ptr(q), _ptr(s), _stream(stream)))
+    _check(lib.mxq_quantize_mxfp8(_ptr(x), R, C, _KIND[kind], _ptr(q), _ptr(s), _LAYOUT[scale_layout],
+                                  _stream(stream)))
     return q, s
 
 
@@ -144,10 +148,10 @@ def nvfp4_workspace_size(rows: int, cols: int) -> int:
     return int(load().mxq_quantize_nvfp4_workspace_size(rows, cols))
 
 
-def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None):
+def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None, scale_layout="row"):
     """bf16 [R, C] -> (packed E2M1 uint8 [R, C/2], E4M3 uint8 [R, C/16], fp32 [1]
     decode scale).  global_scale: None (dynamic, from amax(x)) or a 1-element fp32
-    CUDA tensor (static)."""
+    CUDA tensor (static).  scale_layout as for quantize_mxfp8."""
     torch = _torch()
     _need(x, torch.bfloat16, "x")
     if x.dim() != 2:
@@ -168,8 +172,8 @@ def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None):
             workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=x.device)
         ws_bytes = workspace.numel() * workspace.element_size()
     lib = load()
-    _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _ptr(g),
-                                  _ptr(workspace), ws_bytes, _stream(stream)))
+    _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _LAYOUT[scale_layout],
+                                  _ptr(g), _ptr(workspace), ws_bytes, _stream(stream)))
     return q, s, g
 
 
@@ -231,8 +235,10 @@ def _epi(epi, bias):
     return e
 
 
-def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e4m3", out=None, stream=None):
-    """C[M, N] = epi(A . W^T) in bf16 from MXFP8 operands (A [M, K], W [N, K])."""
+def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e4m3", out=None, stream=None,
+               scale_layout="row"):
+    """C[M, N] = epi(A . W^T) in bf16 from MXFP8 operands (A [M, K], W [N, K]);
+    scale_layout names the order of both scale tensors."""
     torch = _torch()
     for t, n in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, n)
@@ -248,7 +254,7 @@ def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e
     c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
     lib = load()
     _check(lib.mxq_gemm_mxfp8(_ptr(a_q), _ptr(a_s), _KIND[a_kind], _ptr(w_q), _ptr(w_s), _KIND[w_kind],
-                              M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
+                              _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
     return c
 
 
@@ -258,10 +264,11 @@ def gemm_nvfp4_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, workspace=None, split=True,
-               stream=None):
+               stream=None, scale_layout="row"):
     """C[M, N] = epi(s_ga s_gw A . W^T) in bf16 from NVFP4 operands.  With split
     (default), a workspace (given, or allocated here) lets the tiles of a partial
-    last round be split along K."""
+    last round be split along K.  scale_layout names the order of both scale
+    tensors."""
     torch = _torch()
     for t, n in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
         _need(t, torch.uint8, n)
@@ -289,7 +296,8 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, work
             ws = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
             nbytes = need
     _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
-                              M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes, _stream(stream)))
+                              _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes,
+                              _stream(stream)))
     return c
 
 

@@ -20,7 +20,10 @@
 // Tiling: 256 (n) x 256 (m) output tiles, 4 waves in 2 x 2, 128 x 128 per wave
 // (4 x 4 MFMA tiles), K stages of 128 bytes.  Operands and their scale dwords go
 // from global memory straight into LDS (buffer_load ... lds), two stage buffers,
-// XOR-swizzled rows.  Each stage is split at a mid-stage barrier so that one
+// XOR-swizzled rows.  With row-major scales a stage's scale dwords come from 64
+// rows K/32 bytes apart (64 cache lines per load); with the tiled order
+// (TILED, mxq_internal.h) a wave's 64 dwords are one contiguous 256-byte run.
+// Each stage is split at a mid-stage barrier so that one
 // half's MFMAs overlap the other half's fragment reads and the DMA two stages
 // ahead.  The kernel is persistent (one workgroup per CU): a workgroup walks its
 // tiles as one stream of stages, so the next tile's first stages are in flight
@@ -59,7 +62,7 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int R, int x, int S, in
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int AK, int WK, int EPI>
+template <int AK, int WK, int EPI, bool TILED>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N,
@@ -96,6 +99,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   const int wn = wave & 1, wm = wave >> 1;
   int r = lane & 31, g = lane >> 5;
   const int KB = K / 32;            // scale bytes per row
+  const int NST = K / kBK;          // stages per row (TILED: 256-byte runs per 64-row block)
 
   // Buffer resources with 32-bit offsets (operands are < 2 GiB, checked by the host).
   const auto rw = __builtin_amdgcn_make_buffer_rsrc((void*)wq, (short)0, N * K, 0x00020000);
@@ -110,7 +114,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // load and the global chunk that lands at physical chunk i % 8.  Rows 8j + i/8
   // have swz = ((i/8) >> 1) + 4 (j & 1), hence two lane offsets.  The stage's scale
   // dwords (4 MX blocks of every row) follow with one 4-byte-per-lane load per
-  // operand: lane i of wave w -> row 64w + i.
+  // operand: lane i of wave w -> row 64w + i (TILED: dword i of the run of the
+  // wave's 64-row block and this stage).
   int voff0, voff1, vsc;
   // Every load stays inside its operand.  A wave's 64 rows lie wholly inside or
   // wholly past M (N), both being multiples of 128; rows past the end, and the
@@ -121,7 +126,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
     const bool vw = valid && rw0 < N, va = valid && ra0 < M;
     const int off_w = vw ? rw0 * K + k0 : 0, off_a = va ? ra0 * K + k0 : 0;
-    const int off_sw = vw ? rw0 * KB + k0 / 32 : 0, off_sa = va ? ra0 * KB + k0 / 32 : 0;
+    const int st = k0 / kBK;
+    const int off_sw = vw ? (TILED ? ((rw0 >> 6) * NST + st) * 256 : rw0 * KB + k0 / 32) : 0;
+    const int off_sa = va ? (TILED ? ((ra0 >> 6) * NST + st) * 256 : ra0 * KB + k0 / 32) : 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int vo = (j & 1) ? voff1 : voff0;
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     const int cx = lchunk ^ (lrow >> 1);
     voff0 = lrow * K + cx * 16;
     voff1 = lrow * K + (cx ^ 4) * 16;
-    vsc = lane * KB;
+    vsc = TILED ? lane * 4 : lane * KB;
     x = swz(r);
     wrow = wn * 128 + r;
     arow = wm * 128 + r;
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);   // no DMA outlives the workgroup
 }
 
-template <int AK, int WK>
+template <int AK, int WK, bool TILED>
 hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int M, int N, int K,
                         const void* bias, int epi, void* c, hipStream_t stream) {
   const int tiles = ((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile);
@@ -311,9 +318,12 @@ hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const
   auto Ws = (const uint8_t*)w_s;
   auto B = (const uint16_t*)bias;
   auto C = (uint16_t*)c;
-  if (epi == 0) hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 0>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
-  else if (epi == 1) hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 1>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
-  else hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 2>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
+  if (epi == 0)
+    hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 0, TILED>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
+  else if (epi == 1)
+    hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 1, TILED>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
+  else
+    hipLaunchKernelGGL((k_gemm_mxfp8<AK, WK, 2, TILED>), grid, block, 0, stream, A, As, W, Ws, B, C, M, N, K);
   return hipGetLastError();
 }
 
@@ -323,12 +333,18 @@ hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const
 // Partial 256-tiles (M or N = 128 mod 256) skip the stores of their missing half.
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q, const void* w_s,
                              int w_kind, int64_t M, int64_t N, int64_t K, const void* bias, int epi, void* c,
-                             hipStream_t stream) {
+                             bool scales_tiled, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
-  if (a_kind == 0 && w_kind == 0) return launch_kinds<0, 0>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream);
-  if (a_kind == 1 && w_kind == 1) return launch_kinds<1, 1>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream);
-  if (a_kind == 0 && w_kind == 1) return launch_kinds<0, 1>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream);
-  return launch_kinds<1, 0>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream);
+#define MXQ_MX_KINDS(T)                                                                                      \
+  if (a_kind == 0 && w_kind == 0) return launch_kinds<0, 0, T>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream); \
+  if (a_kind == 1 && w_kind == 1) return launch_kinds<1, 1, T>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream); \
+  if (a_kind == 0 && w_kind == 1) return launch_kinds<0, 1, T>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream); \
+  return launch_kinds<1, 0, T>(a_q, a_s, w_q, w_s, m, n, k, bias, epi, c, stream);
+  if (scales_tiled) {
+    MXQ_MX_KINDS(true)
+  }
+  MXQ_MX_KINDS(false)
+#undef MXQ_MX_KINDS
 }
 
 }  // namespace mxq

@@ -33,11 +33,12 @@
 //
 // Scale layout.  The texture unit's work for a load goes by the rows (cache
 // lines) it touches, and a stage needs only 8 scale bytes of each of 64 rows per
-// wave and operand.  Given a workspace, k_tile_scales first rewrites both
-// operands' scales into 64-row blocks, stage by stage ([R/64][K/128][64][8 B]),
-// and the GEMM (TILED) then fetches a stage's scales for its 64 rows as one
-// contiguous 1 KiB load per wave and operand (with the next stage's along).
-// Without one it reads them in place, 16 bytes per row.
+// wave and operand.  In the tiled order of mxq_internal.h ([R/64][K/128][64][8 B],
+// which the quantizer can write directly), the GEMM (TILED) fetches a stage's
+// scales for its 64 rows as one contiguous 1 KiB load per wave and operand (with
+// the next stage's along).  Row-major scales are rewritten into that order by
+// k_tile_scales when a workspace is given, and read in place, 16 bytes per row,
+// when not.
 #include <type_traits>
 
 #include "mxq_internal.h"
@@ -473,7 +474,7 @@ size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // workspace is NULL or holds gemm_nvfp4_workspace_bytes(M, N, K).
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q, const void* w_s,
                              const float* w_g, int64_t M, int64_t N, int64_t K, const void* bias, int epi, void* c,
-                             void* workspace, hipStream_t stream) {
+                             bool scales_tiled, void* workspace, hipStream_t stream) {
   const int m = (int)M, n = (int)N, k = (int)K;
   const int tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
   // persistent (one workgroup per CU) when a tile has an even number of K stages;
@@ -491,9 +492,10 @@ hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g,
   auto As = (const uint8_t*)a_s;
   auto W = (const uint8_t*)w_q;
   auto Ws = (const uint8_t*)w_s;
-  // With a workspace, both operands' scales in the GEMM's layout first.
-  const bool tiled = workspace != nullptr;
-  if (tiled) {
+  // Row-major scales with a workspace: both operands' scales into the GEMM's
+  // layout first.  Scales that come tiled are read in place.
+  const bool tiled = scales_tiled || workspace != nullptr;
+  if (tiled && !scales_tiled) {
     const int KS = k / 16, nst = k / kBK;
     uint8_t* at = (uint8_t*)workspace + round256(gemm_split_bytes(nvfp4_split(M, N, K), tiles));
     uint8_t* wt = at + round256((size_t)M * KS);

@@ -57,6 +57,20 @@ mxq_status launched(hipError_t e, const char* what) {
 
 constexpr int64_t kMax32 = (int64_t)1 << 31;
 
+// Validates a quantizer's scale layout for a [rows, cols] tensor: the tiled order
+// groups rows by 64 and K by 128 values.
+mxq_status check_scale_layout(mxq_scale_layout layout, int64_t rows, int64_t cols) {
+  if (layout != MXQ_SCALES_ROW_MAJOR && layout != MXQ_SCALES_TILED)
+    return fail(MXQ_ERROR_INVALID_VALUE, "bad scale layout %d", (int)layout);
+  if (layout == MXQ_SCALES_TILED && (rows % 64 != 0 || cols % 128 != 0))
+    return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "tiled scales need rows %% 64 == 0 and cols %% 128 == 0 (got %lld, %lld)",
+                (long long)rows, (long long)cols);
+  // one workgroup per 64 x 128 values, numbered with 31 bits (with room to spare)
+  if (layout == MXQ_SCALES_TILED && rows > ((int64_t)1 << 43) / cols)
+    return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "tensor too large for tiled scales");
+  return MXQ_SUCCESS;
+}
+
 std::atomic<int> g_cus[64];
 
 }  // namespace
@@ -72,22 +86,26 @@ int device_compute_units() {
   }
   return n;
 }
+ScaleTiling scale_tiling(int64_t cols) { return ScaleTiling{cols / 8, (int)(cols / 128)}; }
 }  // namespace mxq
 
 extern "C" {
 
 mxq_status mxq_quantize_mxfp8(const void* x, int64_t rows, int64_t cols, mxq_fp8_kind kind, void* q,
-                              void* scales, void* stream) {
+                              void* scales, mxq_scale_layout scale_layout, void* stream) {
   if (!x || !q || !scales) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
   if (rows <= 0 || cols <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "rows and cols must be positive");
   if (kind != MXQ_FP8_E4M3 && kind != MXQ_FP8_E5M2) return fail(MXQ_ERROR_INVALID_VALUE, "bad fp8 kind %d", (int)kind);
   if (cols % 32 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "cols (%lld) must be a multiple of 32", (long long)cols);
   if (rows > INT64_MAX / cols) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "rows * cols overflows");
+  mxq_status l = check_scale_layout(scale_layout, rows, cols);
+  if (l != MXQ_SUCCESS) return l;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
     return fail(MXQ_ERROR_MISALIGNED, "x, q and scales must be 16-byte aligned");
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
-  return launched(mxq::launch_quantize_mxfp8(x, rows * cols, (int)kind, q, scales, (hipStream_t)stream),
+  const mxq::ScaleTiling tiling = mxq::scale_tiling(scale_layout == MXQ_SCALES_TILED ? cols : 0);
+  return launched(mxq::launch_quantize_mxfp8(x, rows * cols, (int)kind, q, scales, tiling, (hipStream_t)stream),
                   "mxq_quantize_mxfp8 launch");
 }
 
@@ -97,12 +115,14 @@ size_t mxq_quantize_nvfp4_workspace_size(int64_t rows, int64_t cols) {
 }
 
 mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, const float* global_scale_in, void* q,
-                              void* scales, float* global_scale_out, void* workspace, size_t ws_bytes,
-                              void* stream) {
+                              void* scales, mxq_scale_layout scale_layout, float* global_scale_out, void* workspace,
+                              size_t ws_bytes, void* stream) {
   if (!x || !q || !scales || !global_scale_out) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
   if (rows <= 0 || cols <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "rows and cols must be positive");
   if (cols % 16 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "cols (%lld) must be a multiple of 16", (long long)cols);
   if (rows > INT64_MAX / cols) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "rows * cols overflows");
+  mxq_status l = check_scale_layout(scale_layout, rows, cols);
+  if (l != MXQ_SUCCESS) return l;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
     return fail(MXQ_ERROR_MISALIGNED, "x, q and scales must be 16-byte aligned");
   if (((uintptr_t)global_scale_out & 3u) || ((uintptr_t)global_scale_in & 3u))
@@ -116,8 +136,9 @@ mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, const f
   }
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
+  const mxq::ScaleTiling tiling = mxq::scale_tiling(scale_layout == MXQ_SCALES_TILED ? cols : 0);
   return launched(mxq::launch_quantize_nvfp4(x, rows * cols, global_scale_in, q, scales, global_scale_out,
-                                             (uint32_t*)workspace, (hipStream_t)stream),
+                                             (uint32_t*)workspace, tiling, (hipStream_t)stream),
                   "mxq_quantize_nvfp4 launch");
 }
 
@@ -244,11 +265,13 @@ mxq_status mxq_gemm_bf16_fp8w(const void* a, const void* w_q, const float* w_sca
 }
 
 mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_kind, const void* w_q,
-                          const void* w_scales, mxq_fp8_kind w_kind, int64_t M, int64_t N, int64_t K,
-                          const void* bias, mxq_epilogue epi, void* c, void* stream) {
+                          const void* w_scales, mxq_fp8_kind w_kind, mxq_scale_layout scale_layout, int64_t M,
+                          int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c, void* stream) {
   if (!a_q || !a_scales || !w_q || !w_scales) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
   if ((a_kind != MXQ_FP8_E4M3 && a_kind != MXQ_FP8_E5M2) || (w_kind != MXQ_FP8_E4M3 && w_kind != MXQ_FP8_E5M2))
     return fail(MXQ_ERROR_INVALID_VALUE, "bad fp8 kind");
+  if (scale_layout != MXQ_SCALES_ROW_MAJOR && scale_layout != MXQ_SCALES_TILED)
+    return fail(MXQ_ERROR_INVALID_VALUE, "bad scale layout %d", (int)scale_layout);
   mxq_status s = check_gemm_common(M, N, K, bias, epi, c, 1, 1);
   if (s != MXQ_SUCCESS) return s;
   if (!aligned16(a_q) || !aligned16(a_scales) || !aligned16(w_q) || !aligned16(w_scales))
@@ -256,7 +279,7 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
   return launched(mxq::launch_gemm_mxfp8(a_q, a_scales, (int)a_kind, w_q, w_scales, (int)w_kind, M, N, K, bias,
-                                         (int)epi, c, (hipStream_t)stream),
+                                         (int)epi, c, scale_layout == MXQ_SCALES_TILED, (hipStream_t)stream),
                   "mxq_gemm_mxfp8 launch");
 }
 
@@ -267,11 +290,13 @@ size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K) {
 }
 
 mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_global, const void* w_q,
-                          const void* w_scales, const float* w_global, int64_t M, int64_t N, int64_t K,
-                          const void* bias, mxq_epilogue epi, void* c, void* workspace, size_t ws_bytes,
-                          void* stream) {
+                          const void* w_scales, const float* w_global, mxq_scale_layout scale_layout, int64_t M,
+                          int64_t N, int64_t K, const void* bias, mxq_epilogue epi, void* c, void* workspace,
+                          size_t ws_bytes, void* stream) {
   if (!a_q || !a_scales || !a_global || !w_q || !w_scales || !w_global)
     return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  if (scale_layout != MXQ_SCALES_ROW_MAJOR && scale_layout != MXQ_SCALES_TILED)
+    return fail(MXQ_ERROR_INVALID_VALUE, "bad scale layout %d", (int)scale_layout);
   mxq_status s = check_gemm_common(M, N, K, bias, epi, c, 1, 2);
   if (s != MXQ_SUCCESS) return s;
   if (!aligned16(a_q) || !aligned16(a_scales) || !aligned16(w_q) || !aligned16(w_scales))
@@ -287,7 +312,7 @@ mxq_status mxq_gemm_nvfp4(const void* a_q, const void* a_scales, const float* a_
   mxq_status d = check_device();
   if (d != MXQ_SUCCESS) return d;
   return launched(mxq::launch_gemm_nvfp4(a_q, a_scales, a_global, w_q, w_scales, w_global, M, N, K, bias, (int)epi,
-                                         c, workspace, (hipStream_t)stream),
+                                         c, scale_layout == MXQ_SCALES_TILED, workspace, (hipStream_t)stream),
                   "mxq_gemm_nvfp4 launch");
 }
 

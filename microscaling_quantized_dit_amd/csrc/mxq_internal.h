@@ -9,15 +9,25 @@ namespace mxq {
 // Compute units of the current device (cached per device; 256 on MI355X).
 int device_compute_units();
 
+// Block scales in the GEMM-tiled order: the scales of a [rows, cols] tensor stored
+// as [rows / 64][cols / 128][64 rows][P bytes], P = scales per 128 values (4 for
+// MXFP8, 8 for NVFP4); rows % 64 == 0, cols % 128 == 0, rows * cols < 2^43.
+// The quantizers take nst = 0 for row-major scales.
+struct ScaleTiling {
+  int64_t cpr;  // 16-byte chunks (8 values) per row
+  int nst;      // 128-value steps per row; 0 = row-major scales
+};
+ScaleTiling scale_tiling(int64_t cols);   // cols 0 -> row-major
+
 // Host-side launchers (each returns the hipError_t of its launch).
 hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void* q, void* scales,
-                                 hipStream_t stream);
+                                 ScaleTiling tiling, hipStream_t stream);
 
 // Workgroups (= partial maxima) the NVFP4 amax pass uses for n_elems.
 int nvfp4_amax_partials(int64_t n_elems);
 hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* global_in, void* q,
                                  void* scales, float* global_out, uint32_t* partials,
-                                 hipStream_t stream);
+                                 ScaleTiling tiling, hipStream_t stream);
 
 // running = max(running, RN_fp32(amax(x) / 2688)); partials as for the quantizer.
 hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running, uint32_t* partials,
@@ -65,15 +75,17 @@ hipError_t launch_attention_fp8(const void* q, const float* q_scale, const void*
 hipError_t launch_gemm_w8(const void* a, const void* w_q, const float* w_scale, int64_t M, int64_t N, int64_t K,
                           const void* bias, int epi, void* c, hipStream_t stream);
 
+// scales_tiled: both operands' scales in the tiled order above (else row-major)
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q,
                              const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
-                             const void* bias, int epi, void* c, hipStream_t stream);
+                             const void* bias, int epi, void* c, bool scales_tiled, hipStream_t stream);
 
 // workspace: NULL (no split) or at least gemm_nvfp4_workspace_bytes(M, N, K) bytes
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q,
                              const void* w_s, const float* w_g, int64_t M, int64_t N, int64_t K,
-                             const void* bias, int epi, void* c, void* workspace, hipStream_t stream);
+                             const void* bias, int epi, void* c, bool scales_tiled, void* workspace,
+                             hipStream_t stream);
 
 }  // namespace mxq
 
@@ -96,6 +108,28 @@ __device__ __forceinline__ void store_nt(uint2 v, uint2* p) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, v), (u32x2_t*)p);
 }
 __device__ __forceinline__ void store_nt(uint32_t v, uint32_t* p) { __builtin_nontemporal_store(v, p); }
+
+// Work split of the quantizers when they write tiled scales: workgroup b takes the
+// 16 U rows from row 16 U (b / nst) on, columns [128 st, 128 st + 128) with
+// st = b % nst, and thread t the 16-byte chunk t % 16 of that step in rows
+// t / 16 + 16 u, u < U (16 U divides 64).  A wave's 64 lanes then cover four
+// consecutive rows of one step: their scales are one contiguous run of the tiled
+// order.  chunk(u) is the row-major chunk index, scale(u) + lane's block in the
+// run the byte offset of the scale of row t / 16 + 16 u (P scales per row and step).
+template <int U, int P>
+struct TiledSlab {
+  int64_t chunk0;  // chunk of the thread's first row
+  int64_t scale0;  // scale run offset of the thread's first row
+  int64_t cpr;
+  __device__ __forceinline__ TiledSlab(int b, int t, const mxq::ScaleTiling& tl) : cpr(tl.cpr) {
+    const int g = b / tl.nst, st = b - g * tl.nst;
+    const int64_t row = (int64_t)g * (16 * U) + (t >> 4);
+    chunk0 = row * tl.cpr + (int64_t)st * 16 + (t & 15);
+    scale0 = ((row >> 6) * tl.nst + st) * (64 * P) + (row & 63) * P + (t & 15) / (16 / P);
+  }
+  __device__ __forceinline__ int64_t chunk(int u) const { return chunk0 + (int64_t)(16 * u) * cpr; }
+  __device__ __forceinline__ int64_t scale(int u) const { return scale0 + 16 * u * P; }
+};
 
 // Max of the 15-bit magnitudes of the eight bf16 values in a uint4, as a
 // packed pair (the caller folds the halves).  Integer order of bf16 magnitude

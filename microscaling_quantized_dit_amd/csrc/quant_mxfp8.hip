@@ -11,6 +11,9 @@
 // HBM-bound, one pass.  The tensor is treated as a flat stream (cols % 32 == 0,
 // so blocks never straddle rows and the scale of element e is scales[e / 32]),
 // read and written with streaming (nt) accesses: each byte is touched once.
+// Scales go out row-major or in the GEMM-tiled order (mxq_internal.h); for the
+// latter a workgroup takes 64 rows x 128 values, four rows per wave, so that
+// each wave's scale bytes form one contiguous run.
 // Each lane takes 8 consecutive values (one 16-byte load), four neighbouring
 // lanes form a 32-block and find its amax with two cross-lane max steps.
 // x / 2^E is exact in fp32 (2^-E is a normal fp32 for every reachable E), and
@@ -25,6 +28,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 2;  // 16-byte chunks per lane, kept in flight together
+constexpr int kUnrollTiled = 4;   // with tiled scales: 64 rows x 128 values per workgroup
 
 template <int KIND>
 struct Fp8Traits;
@@ -70,20 +74,26 @@ __device__ __forceinline__ int encode4(uint32_t w0, uint32_t w1, float inv) {
   return T::template cvt<true>(f2, f3, r);
 }
 
-template <int KIND>
+// TILED: scales in the GEMM-tiled order, with the work split of dev::TiledSlab
+// (every chunk in range); else the tensor is a flat stream of chunks.
+template <int KIND, bool TILED>
 __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restrict__ x, int64_t n_chunks,
-                                                          uint2* __restrict__ q, uint8_t* __restrict__ s) {
+                                                          uint2* __restrict__ q, uint8_t* __restrict__ s,
+                                                          ScaleTiling tiling) {
+  constexpr int U = TILED ? kUnrollTiled : kUnroll;
   const int t = threadIdx.x;
-  const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll);
-  uint4 v[kUnroll];
+  const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
+  const dev::TiledSlab<U, 4> ts(TILED ? (int)blockIdx.x : 0, t, tiling);
+  auto chunk = [&](int u) { return TILED ? ts.chunk(u) : base + u * kThreads + t; };
+  uint4 v[U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    int64_t c = base + u * kThreads + t;
-    v[u] = c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = chunk(u);
+    v[u] = TILED || c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t c = base + u * kThreads + t;
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = chunk(u);
     // Lanes 4j..4j+3 hold chunks 4j'..4j'+3 of one 32-block (n_chunks % 4 == 0,
     // so a group is entirely in or entirely out of range).
     uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
@@ -94,9 +104,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
     uint2 out;
     out.x = (uint32_t)encode4<KIND>(v[u].x, v[u].y, inv);
     out.y = (uint32_t)encode4<KIND>(v[u].z, v[u].w, inv);
-    if (c < n_chunks) {
+    if (TILED || c < n_chunks) {
       dev::store_nt(out, q + c);
-      if ((t & 3) == 0) s[c >> 2] = (uint8_t)(E + 127);
+      if ((t & 3) == 0) s[TILED ? ts.scale(u) : c >> 2] = (uint8_t)(E + 127);
     }
   }
 }
@@ -104,17 +114,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
 }  // namespace
 
 hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void* q, void* scales,
-                                 hipStream_t stream) {
+                                 ScaleTiling tiling, hipStream_t stream) {
   const int64_t n_chunks = n_elems / 8;
-  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t per_wg = (int64_t)kThreads * (tiling.nst ? kUnrollTiled : kUnroll);
   const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (kind == 0)
-    hipLaunchKernelGGL(k_quant_mxfp8<0>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       (const uint4*)x, n_chunks, (uint2*)q, (uint8_t*)scales);
-  else
-    hipLaunchKernelGGL(k_quant_mxfp8<1>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                       (const uint4*)x, n_chunks, (uint2*)q, (uint8_t*)scales);
+  const dim3 g((unsigned)grid), b(kThreads);
+  auto X = (const uint4*)x;
+  auto Q = (uint2*)q;
+  auto S = (uint8_t*)scales;
+  if (tiling.nst) {
+    if (kind == 0) hipLaunchKernelGGL((k_quant_mxfp8<0, true>), g, b, 0, stream, X, n_chunks, Q, S, tiling);
+    else hipLaunchKernelGGL((k_quant_mxfp8<1, true>), g, b, 0, stream, X, n_chunks, Q, S, tiling);
+  } else {
+    if (kind == 0) hipLaunchKernelGGL((k_quant_mxfp8<0, false>), g, b, 0, stream, X, n_chunks, Q, S, tiling);
+    else hipLaunchKernelGGL((k_quant_mxfp8<1, false>), g, b, 0, stream, X, n_chunks, Q, S, tiling);
+  }
   return hipGetLastError();
 }
 

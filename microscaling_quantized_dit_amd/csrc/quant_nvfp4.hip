@@ -15,7 +15,9 @@
 // way.  (Ordinary loads in the amax pass, leaving a tensor of up to 256 MB in the
 // last-level cache for the encode pass, measured faster in isolation but 10 us
 // slower at 113 MB right after the step's GEMMs.)  The encode pass still takes
-// the slabs last to first.
+// the slabs last to first.  Block scales go out row-major or in the GEMM-tiled
+// order (mxq_internal.h); for the latter a workgroup takes 64 rows x 128 values,
+// four rows per wave, so that each wave's scale bytes form one contiguous run.
 //
 // Exact rounding at HBM speed.  Both quotients above are inexact in fp32, so
 // each is evaluated twice, with the divisor's reciprocal nudged down and up by
@@ -172,22 +174,29 @@ __device__ __forceinline__ uint32_t encode8(uint4 v, float r) {
   return out;
 }
 
+// TILED: scales in the GEMM-tiled order, with the work split of dev::TiledSlab
+// (64 rows x 128 values per workgroup, every chunk in range); else the tensor is
+// a flat stream of chunks.
+template <bool TILED>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restrict__ x, int64_t n_chunks,
                                                           const float* __restrict__ global_in,
                                                           const uint32_t* __restrict__ partials, int n_partials,
                                                           uint32_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                          float* __restrict__ global_out, int reverse) {
+                                                          float* __restrict__ global_out, int reverse,
+                                                          ScaleTiling tiling) {
   __shared__ uint32_t red[kThreads / 64];
   const int t = threadIdx.x;
   // with `reverse` workgroups take the slabs last to first: right after the amax
   // pass, what it read last is the likeliest to be left in a cache
   const int64_t slab = reverse ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
   const int64_t base = slab * (kThreads * kUnroll);
+  const dev::TiledSlab<kUnroll, 8> ts(TILED ? (int)slab : 0, t, tiling);
+  auto chunk = [&](int u) { return TILED ? ts.chunk(u) : base + u * kThreads + t; };
   uint4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    int64_t c = base + u * kThreads + t;
-    v[u] = c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
+    const int64_t c = chunk(u);
+    v[u] = TILED || c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
   }
 
   // ---- the global decode scale s_g
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
 
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const int64_t c = base + u * kThreads + t;
+    const int64_t c = chunk(u);
     // lanes 2j, 2j+1 hold the two halves of one 16-block (n_chunks is even)
     uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
     m = max(m, (uint32_t)__shfl_xor((int)m, 1));
@@ -249,9 +258,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
     const bool slow = S != 0.0f && (!(D >= 0x1p-100f) || sb == 126);
     if (__builtin_expect(slow, 0)) codes = exact_chunk(v[u], S, sg);
     else if (__builtin_expect(S != 0.0f && codes != hi, 0)) codes = resolve_chunk(v[u], codes, hi, S, sg);
-    if (c < n_chunks) {
+    if (TILED || c < n_chunks) {
       dev::store_nt(codes, q + c);
-      if ((t & 1) == 0) s[c >> 1] = (uint8_t)sb;
+      if ((t & 1) == 0) s[TILED ? ts.scale(u) : c >> 1] = (uint8_t)sb;
     }
   }
 }
@@ -477,7 +486,7 @@ int nvfp4_amax_partials(int64_t n_elems) {
 
 hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* global_in, void* q,
                                  void* scales, float* global_out, uint32_t* partials,
-                                 hipStream_t stream) {
+                                 ScaleTiling tiling, hipStream_t stream) {
   const int64_t n_chunks = n_elems / 8;
   int n_partials = 0;
   if (!global_in) {
@@ -485,12 +494,16 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* gl
     hipError_t e = amax_pass(x, n_chunks, partials, n_partials, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t per_wg = (int64_t)kThreads * kUnroll;
+  const int64_t per_wg = (int64_t)kThreads * kUnroll;   // = 64 rows x 128 values when tiled
   const int64_t grid = (n_chunks + per_wg - 1) / per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_quant_nvfp4, dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x,
-                     n_chunks, global_in, partials, n_partials, (uint32_t*)q, (uint8_t*)scales, global_out,
-                     global_in ? 0 : 1);
+#define MXQ_NV_QUANT(T)                                                                                     \
+  hipLaunchKernelGGL((k_quant_nvfp4<T>), dim3((unsigned)grid), dim3(kThreads), 0, stream, (const uint4*)x,   \
+                     n_chunks, global_in, partials, n_partials, (uint32_t*)q, (uint8_t*)scales, global_out, \
+                     global_in ? 0 : 1, tiling)
+  if (tiling.nst) MXQ_NV_QUANT(true);
+  else MXQ_NV_QUANT(false);
+#undef MXQ_NV_QUANT
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ FAKE2 = 0x20000
 MIS = 0x10008           # 8 mod 16
 
 SUCCESS, INVALID, SHAPE, MISALIGNED, WORKSPACE, DEVICE, LAUNCH = range(7)
+ROW, TILED = 0, 1
 
 
 @pytest.fixture(scope="module")
@@ -56,8 +57,8 @@ def test_status_strings(lib):
         assert word in lib.mxq_status_string(code)
 
 
-def _q8(lib, x=FAKE, rows=4, cols=64, kind=0, q=FAKE, s=FAKE2):
-    return lib.mxq_quantize_mxfp8(x, rows, cols, kind, q, s, None)
+def _q8(lib, x=FAKE, rows=4, cols=64, kind=0, q=FAKE, s=FAKE2, layout=ROW):
+    return lib.mxq_quantize_mxfp8(x, rows, cols, kind, q, s, layout, None)
 
 
 def test_quantize_mxfp8_validation(lib):
@@ -71,6 +72,12 @@ def test_quantize_mxfp8_validation(lib):
     assert _q8(lib, x=MIS) == MISALIGNED
     assert _q8(lib, s=MIS) == MISALIGNED
     assert b"multiple of 32" in (_q8(lib, cols=48) and lib.mxq_last_error())
+    # the tiled scale order groups rows by 64 and K by 128
+    assert _q8(lib, layout=2) == INVALID
+    assert _q8(lib, layout=TILED) == SHAPE                      # 4 rows
+    assert _q8(lib, rows=64, cols=96, layout=TILED) == SHAPE
+    assert _q8(lib, rows=64, cols=128, layout=TILED, s=MIS) == MISALIGNED
+    assert _q8(lib, rows=1 << 37, cols=1 << 7, layout=TILED) == SHAPE   # workgroups past 2^31
 
 
 def test_quantize_nvfp4_validation(lib):
@@ -78,8 +85,8 @@ def test_quantize_nvfp4_validation(lib):
     assert ws(128, 256) >= 4 and ws(128, 24) == 0 and ws(0, 16) == 0
     need = ws(4, 64)
 
-    def call(x=FAKE, rows=4, cols=64, gin=None, q=FAKE, s=FAKE2, gout=FAKE, w=FAKE2, wsb=need):
-        return lib.mxq_quantize_nvfp4(x, rows, cols, gin, q, s, gout, w, wsb, None)
+    def call(x=FAKE, rows=4, cols=64, gin=None, q=FAKE, s=FAKE2, gout=FAKE, w=FAKE2, wsb=need, layout=ROW):
+        return lib.mxq_quantize_nvfp4(x, rows, cols, gin, q, s, layout, gout, w, wsb, None)
 
     assert call(x=None) == INVALID
     assert call(gout=None) == INVALID
@@ -89,6 +96,9 @@ def test_quantize_nvfp4_validation(lib):
     assert call(gout=FAKE + 2) == MISALIGNED
     assert call(w=None) == WORKSPACE
     assert call(wsb=need - 4) == WORKSPACE
+    assert call(layout=-1) == INVALID
+    assert call(layout=TILED) == SHAPE
+    assert call(rows=128, cols=64, layout=TILED) == SHAPE
 
 
 def test_nvfp4_calibrate_validation(lib):
@@ -133,8 +143,8 @@ def test_fp8_weight_validation(lib):
     assert gemm() == DEVICE
 
 
-def _g8(lib, M=128, N=256, K=256, bias=None, epi=0, c=FAKE, a=FAKE, ak=0, wk=0):
-    return lib.mxq_gemm_mxfp8(a, FAKE2, ak, FAKE, FAKE2, wk, M, N, K, bias, epi, c, None)
+def _g8(lib, M=128, N=256, K=256, bias=None, epi=0, c=FAKE, a=FAKE, ak=0, wk=0, layout=ROW):
+    return lib.mxq_gemm_mxfp8(a, FAKE2, ak, FAKE, FAKE2, wk, layout, M, N, K, bias, epi, c, None)
 
 
 def test_gemm_mxfp8_validation(lib):
@@ -149,16 +159,20 @@ def test_gemm_mxfp8_validation(lib):
     assert _g8(lib, M=1 << 20, K=1 << 12) == SHAPE  # A would exceed 2 GiB
     assert _g8(lib, c=MIS) == MISALIGNED
     assert _g8(lib, epi=2, bias=MIS) == MISALIGNED
+    assert _g8(lib, layout=7) == INVALID
+    assert _g8(lib, layout=TILED, K=192) == SHAPE
 
 
 def test_gemm_nvfp4_validation(lib):
-    def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE, ws=None, nbytes=0):
-        return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, M, N, K, bias, epi, c, ws, nbytes, None)
+    def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE, ws=None, nbytes=0, layout=ROW):
+        return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, layout, M, N, K, bias, epi, c, ws, nbytes,
+                                  None)
 
     assert call(ag=None) == INVALID
     assert call(N=100) == SHAPE
     assert call(epi=2) == INVALID
     assert call(ag=FAKE + 1) == MISALIGNED
+    assert call(layout=2) == INVALID
     # a shape with a partial last round (17 x 16 tiles on 256 compute units, the
     # count assumed without a device) wants a workspace; too small a one is refused
     def scales(M, N, K):                                 # both operands' scales, re-laid out
@@ -199,7 +213,9 @@ def test_attention_validation(lib):
 def test_device_gate_without_gpu(lib):
     """Valid arguments reach the device check, which refuses without a gfx950."""
     assert _q8(lib) == DEVICE
+    assert _q8(lib, rows=64, cols=128, layout=TILED) == DEVICE
     assert _g8(lib) == DEVICE
+    assert _g8(lib, layout=TILED) == DEVICE
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -191,6 +191,80 @@ def test_nvfp4_scale_layouts_agree(mxq, M, N, K):
     _assert_close(_bf16_out(c1), r, "nv layouts %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (384, 640, 256), (640, 384, 1152), (4608, 3072, 3072)])
+def test_mxfp8_tiled_scales(mxq, M, N, K):
+    """The MXFP8 GEMM reading both operands' scales in the tiled order gives the
+    bits of the row-major read (same products, same order), for mixed element
+    formats and the bias + GELU epilogue, and matches the oracle."""
+    import torch
+    from tests.test_gpu_quant import tile_scales
+    A = MX(inputs.flux_activation(M, K, seed=K, stream="tiled/A"), oracle.E4M3)
+    W = MX(inputs.weight(N, K, seed=K, stream="tiled/W"), oracle.E5M2)
+    b = inputs.bias(N, K, seed=K, stream="tiled/b")
+    db = inputs.to_torch(b, "cuda")
+    ta, tw = _t(tile_scales(A.s, 4)), _t(tile_scales(W.s, 4))
+    c1 = mxq.gemm_mxfp8(A.dq, ta, W.dq, tw, bias=db, epi="bias_gelu", a_kind="e4m3", w_kind="e5m2",
+                        scale_layout="tiled")
+    c2 = mxq.gemm_mxfp8(A.dq, A.ds, W.dq, W.ds, bias=db, epi="bias_gelu", a_kind="e4m3", w_kind="e5m2")
+    assert torch.equal(c1, c2)
+    rows = None if M * N <= 1 << 20 else np.arange(0, M, 97)
+    r = oracle.gemm_mxfp8(A.q, A.s, W.q, W.s, A.fmt, W.fmt, bias=b, epi=oracle.EPI_BIAS_GELU_TANH, row_idx=rows)
+    g = _bf16_out(c1)
+    _assert_close(g if rows is None else g[rows], r, "mx tiled %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(384, 640, 256), (640, 384, 1152), (4352, 4096, 1024)])
+def test_nvfp4_tiled_scales(mxq, M, N, K):
+    """Scales handed to the NVFP4 GEMM already tiled are read in place: with a
+    workspace (split tiles at 4352 x 4096 x 1024) the result is the bits of the
+    row-major call with the same workspace; without one, of the row-major call
+    without one; and it matches the oracle."""
+    import torch
+    from tests.test_gpu_quant import tile_scales
+    A = NV(inputs.flux_activation(M, K, seed=K, stream="tiled/A"))
+    W = NV(inputs.weight(N, K, seed=K, stream="tiled/W"))
+    b = inputs.bias(N, K, seed=K, stream="tiled/b")
+    db = inputs.to_torch(b, "cuda")
+    ta, tw = _t(tile_scales(A.s, 8)), _t(tile_scales(W.s, 8))
+    ws = torch.empty((mxq.gemm_nvfp4_workspace_size(M, N, K),), dtype=torch.uint8, device="cuda")
+    args = dict(bias=db, epi="bias_gelu")
+    c1 = mxq.gemm_nvfp4(A.dq, ta, A.dg, W.dq, tw, W.dg, workspace=ws, scale_layout="tiled", **args)
+    c2 = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, workspace=ws, **args)
+    assert torch.equal(c1, c2)
+    c3 = mxq.gemm_nvfp4(A.dq, ta, A.dg, W.dq, tw, W.dg, split=False, scale_layout="tiled", **args)
+    c4 = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, split=False, **args)
+    assert torch.equal(c3, c4)
+    rows = None if M * N <= 1 << 20 else np.arange(0, M, 61)
+    r = oracle.gemm_nvfp4(A.q, A.s, A.g, W.q, W.s, W.g, bias=b, epi=oracle.EPI_BIAS_GELU_TANH, row_idx=rows)
+    for c in (c1, c3):
+        g = _bf16_out(c)
+        _assert_close(g if rows is None else g[rows], r, "nv tiled %dx%dx%d" % (M, N, K))
+
+
+def test_tiled_quantizer_to_gemm(mxq):
+    """The chain the FLUX step runs: GPU quantizers writing tiled scales straight
+    into the GEMMs, against the same chain with row-major scales."""
+    import torch
+    M, N, K = 512, 768, 1536
+    x = inputs.to_torch(inputs.flux_activation(M, K, seed=3, stream="chain/x"), "cuda")
+    w = inputs.to_torch(inputs.weight(N, K, seed=3, stream="chain/w"), "cuda")
+    for lay in ("row", "tiled"):
+        aq, as_ = mxq.quantize_mxfp8(x, scale_layout=lay)
+        wq, ws_ = mxq.quantize_mxfp8(w, scale_layout=lay)
+        c = mxq.gemm_mxfp8(aq, as_, wq, ws_, scale_layout=lay)
+        if lay == "row":
+            c_mx = c
+        else:
+            assert torch.equal(c, c_mx)
+        aq, as_, ag = mxq.quantize_nvfp4(x, scale_layout=lay)
+        wq, ws_, wg = mxq.quantize_nvfp4(w, scale_layout=lay)
+        c = mxq.gemm_nvfp4(aq, as_, ag, wq, ws_, wg, scale_layout=lay)
+        if lay == "row":
+            c_nv = c
+        else:
+            assert torch.equal(c, c_nv)
+
+
 def test_deterministic(mxq):
     import torch
     A = NV(inputs.flux_activation(512, 1024, seed=2, stream="det/A"))

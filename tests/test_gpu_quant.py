@@ -169,6 +169,66 @@ def test_deterministic(mxq):
         assert torch.equal(u, v)
 
 
+# --------------------------------------------------- tiled scale order
+
+def tile_scales(s, per_step):
+    """Row-major [R, J] block scales -> the GEMM-tiled byte order, written here as
+    a reshape: rows in blocks of 64, scales in steps of per_step (128 K values),
+    each (row block, step) one run of 64 rows x per_step bytes.  Same shape back."""
+    R, J = s.shape
+    return np.ascontiguousarray(
+        s.reshape(R // 64, 64, J // per_step, per_step).transpose(0, 2, 1, 3)).reshape(R, J)
+
+
+def test_tile_scales_helper():
+    """The reshape above against the offset formula, element by element."""
+    R, J, P = 128, 24, 4
+    s = np.arange(R * J, dtype=np.int64).reshape(R, J)
+    t = tile_scales(s, P).reshape(-1)
+    for r in range(R):
+        for j in range(J):
+            assert t[((r // 64) * (J // P) + j // P) * 64 * P + (r % 64) * P + j % P] == s[r, j]
+
+
+@pytest.mark.parametrize("shape", [(64, 128), (192, 640), (128, 3200), (320, 1152)])
+def test_tiled_scales_match_oracle(mxq, shape):
+    """Both quantizers with the tiled scale order: codes as in the row-major
+    order, scales the oracle's in the tiled order, bit for bit."""
+    import torch
+    x = inputs.flux_activation(*shape, seed=11, stream="tiled")
+    dx = _dev(x)
+    for kind, fmt in KINDS:
+        q, s = mxq.quantize_mxfp8(dx, kind, scale_layout="tiled")
+        rq, rs = oracle.quantize_mxfp8(x, fmt)
+        np.testing.assert_array_equal(_np(q), rq)
+        np.testing.assert_array_equal(_np(s), tile_scales(rs, 4))
+    for static in (None, 0.25):
+        gin = None if static is None else torch.tensor([static], dtype=torch.float32, device="cuda")
+        q, s, g = mxq.quantize_nvfp4(dx, global_scale=gin, scale_layout="tiled")
+        rg = oracle.nvfp4_global_scale(x) if static is None else np.float32(static)
+        rq, rs, _ = oracle.quantize_nvfp4(x, global_scale=rg)
+        assert np.float32(_np(g)[0]).tobytes() == np.float32(rg).tobytes()
+        np.testing.assert_array_equal(_np(q), rq)
+        np.testing.assert_array_equal(_np(s), tile_scales(rs, 8))
+
+
+@pytest.mark.parametrize("rows,cols", [(4608, 12288), (18432, 15360)])
+def test_tiled_scales_full_size(mxq, rows, cols):
+    """At the FLUX activation shapes (18432 x 15360 has 17.7 M NVFP4 scales): the
+    tiled scales are the row-major ones reordered, every byte."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(rows + cols)
+    x = (torch.randn((rows, cols), generator=gen, device="cuda") * 3).to(torch.bfloat16)
+    _, s_row = mxq.quantize_mxfp8(x)
+    _, s_til = mxq.quantize_mxfp8(x, scale_layout="tiled")
+    np.testing.assert_array_equal(_np(s_til), tile_scales(_np(s_row), 4))
+    del s_row, s_til
+    q_row, s_row, g_row = mxq.quantize_nvfp4(x)
+    q_til, s_til, g_til = mxq.quantize_nvfp4(x, scale_layout="tiled")
+    assert torch.equal(q_row, q_til) and torch.equal(g_row, g_til)
+    np.testing.assert_array_equal(_np(s_til), tile_scales(_np(s_row), 8))
+
+
 # ------------------------------------- static-scale calibration (P5 step 1)
 
 def test_nvfp4_static_calibration(mxq):
