@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from microscaling_quantized_dit_amd import inputs
+from tests.scale_order import tile_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -53,17 +54,30 @@ class NV:
         self.dg = _t(np.array([self.g], np.float32))
 
 
-def run_mx(mxq, A, W, bias=None, epi="none", rows=None):
-    c = mxq.gemm_mxfp8(A.dq, A.ds, W.dq, W.ds, bias=None if bias is None else inputs.to_torch(bias, "cuda"),
-                       epi=epi, a_kind=A.kind, w_kind=W.kind)
+def run_mx(mxq, A, W, bias=None, epi="none", rows=None, layout="row"):
+    """layout "tiled": the scales handed over in the GEMM-tiled order, and the
+    result also required bit-identical to the row-major call's."""
+    db = None if bias is None else inputs.to_torch(bias, "cuda")
+    c = mxq.gemm_mxfp8(A.dq, A.ds, W.dq, W.ds, bias=db, epi=epi, a_kind=A.kind, w_kind=W.kind)
+    if layout == "tiled":
+        ct = mxq.gemm_mxfp8(A.dq, _t(tile_scales(A.s, 4)), W.dq, _t(tile_scales(W.s, 4)), bias=db, epi=epi,
+                            a_kind=A.kind, w_kind=W.kind, scale_layout="tiled")
+        assert (ct == c).all().item()
+        c = ct
     g = _bf16_out(c)
     r = oracle.gemm_mxfp8(A.q, A.s, W.q, W.s, A.fmt, W.fmt, bias=bias, epi=EPIS[epi], row_idx=rows)
     return (g if rows is None else g[rows]), r
 
 
-def run_nv(mxq, A, W, bias=None, epi="none", rows=None):
-    c = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg,
-                       bias=None if bias is None else inputs.to_torch(bias, "cuda"), epi=epi)
+def run_nv(mxq, A, W, bias=None, epi="none", rows=None, layout="row"):
+    """layout as for run_mx (both calls with the default workspace)."""
+    db = None if bias is None else inputs.to_torch(bias, "cuda")
+    c = mxq.gemm_nvfp4(A.dq, A.ds, A.dg, W.dq, W.ds, W.dg, bias=db, epi=epi)
+    if layout == "tiled":
+        ct = mxq.gemm_nvfp4(A.dq, _t(tile_scales(A.s, 8)), A.dg, W.dq, _t(tile_scales(W.s, 8)), W.dg, bias=db,
+                            epi=epi, scale_layout="tiled")
+        assert (ct == c).all().item()
+        c = ct
     g = _bf16_out(c)
     r = oracle.gemm_nvfp4(A.q, A.s, A.g, W.q, W.s, W.g, bias=bias, epi=EPIS[epi], row_idx=rows)
     return (g if rows is None else g[rows]), r
@@ -197,7 +211,6 @@ def test_mxfp8_tiled_scales(mxq, M, N, K):
     bits of the row-major read (same products, same order), for mixed element
     formats and the bias + GELU epilogue, and matches the oracle."""
     import torch
-    from tests.test_gpu_quant import tile_scales
     A = MX(inputs.flux_activation(M, K, seed=K, stream="tiled/A"), oracle.E4M3)
     W = MX(inputs.weight(N, K, seed=K, stream="tiled/W"), oracle.E5M2)
     b = inputs.bias(N, K, seed=K, stream="tiled/b")
@@ -220,7 +233,6 @@ def test_nvfp4_tiled_scales(mxq, M, N, K):
     row-major call with the same workspace; without one, of the row-major call
     without one; and it matches the oracle."""
     import torch
-    from tests.test_gpu_quant import tile_scales
     A = NV(inputs.flux_activation(M, K, seed=K, stream="tiled/A"))
     W = NV(inputs.weight(N, K, seed=K, stream="tiled/W"))
     b = inputs.bias(N, K, seed=K, stream="tiled/b")
@@ -284,22 +296,24 @@ def _rows(M, n, seed):
 @pytest.mark.parametrize("name,N,K,epi", [("qkv", 9216, 3072, "none"), ("out", 3072, 3072, "none"),
                                           ("mlp_up", 12288, 3072, "bias_gelu"), ("mlp_down", 3072, 12288, "none")])
 def test_flux_double_stream_mxfp8(mxq, name, N, K, epi):
-    """FLUX double-stream linears at M = 4608 tokens, MXFP8 E4M3; 64 sampled rows."""
+    """FLUX double-stream linears at M = 4608 tokens, MXFP8 E4M3; 64 sampled rows.
+    Tiled scales, as the bench step runs them (and row-major, bit-identical)."""
     M = 4608
     A = MX(inputs.flux_activation(M, K, seed=0, stream="cfg3/%s/A" % name), oracle.E4M3)
     W = MX(inputs.weight(N, K, seed=0, stream="cfg3/%s/W" % name), oracle.E4M3)
     b = inputs.bias(N, K, seed=0, stream="cfg3/%s/b" % name) if epi != "none" else None
-    _assert_close(*run_mx(mxq, A, W, bias=b, epi=epi, rows=_rows(M, 64, 1)), name)
+    _assert_close(*run_mx(mxq, A, W, bias=b, epi=epi, rows=_rows(M, 64, 1), layout="tiled"), name)
 
 
 @pytest.mark.parametrize("name,N,K", [("linear1", 21504, 3072), ("linear2", 3072, 15360)])
 def test_flux_single_stream_nvfp4(mxq, name, N, K):
     """FLUX single-stream linears at batch 4 (M = 18432), NVFP4 with a dynamic
-    activation scale; 32 sampled rows."""
+    activation scale; 32 sampled rows.  Tiled scales and a workspace (linear2's
+    partial last round split along K), as the bench step runs them."""
     M = 18432
     A = NV(inputs.flux_activation(M, K, seed=0, stream="cfg4/%s/A" % name))
     W = NV(inputs.weight(N, K, seed=0, stream="cfg4/%s/W" % name))
-    _assert_close(*run_nv(mxq, A, W, rows=_rows(M, 32, 2)), name)
+    _assert_close(*run_nv(mxq, A, W, rows=_rows(M, 32, 2), layout="tiled"), name)
 
 
 @pytest.mark.parametrize("N", [4096, 16384])
