@@ -158,12 +158,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   // all four loads of a wave's 64 rows.  Scales: lane i -> row 64w + i, 16 bytes
   // from the stage's first block on (the stage's 8 bytes and the next stage's,
   // which are not used: one 16-byte load per row costs the texture unit half of
-  // what two 4-byte loads do; past the end of the operand the load returns zeros).
+  // what two 4-byte loads do).  TILED: lane i -> bytes [16i, 16i + 16) of the
+  // stage's 512-byte run and the next one.  At the last stage the load reaches 8
+  // (row-major) or 512 (TILED) bytes past the end of the operand; the buffer
+  // resource's bound returns zeros there, and those bytes are never used.
   int voff = (lane >> 2) * KP + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
   int vsc = TILED ? lane * 16 : lane * KS;
   // Every code load stays inside its operand: a wave's 64 rows lie wholly inside
   // or past M (N); rows past the end, and stages after the last tile, read rows
-  // [0, 64).  (A scale load can reach 8 bytes past the end, see above.)
+  // [0, 64).  (A scale load can reach past the end, see above.)
   // Part p (0..3) of a stage's DMA: code rows 16p..16p+15 of this wave's 64 for W
   // and A, and in parts 0 and 1 the W and the A scale load.  The parts
   // are issued a quarter of a phase apart so that the four waves' loads reach the
