@@ -285,8 +285,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   auto epilogue = [&](const v16f (&acc)[4][4], int m0, int n0) {
     // M and N are multiples of 128: a wave's 128 x 128 block is wholly in or out
     if (m0 + wm * 128 >= M || n0 + wn * 128 >= N) return;
+    // a fresh lane id (opaque to the compiler): nothing lane-derived stays live
+    // across the K loop for the epilogue's sake
+    int el;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(el));
     dev::epilogue_block<EPI, 128, true>(acc, alpha, bias_lds + wave * 1024, c_lds + wave * kCStage, c, N,
-                                        m0 + wm * 128, n0 + wn * 128, lane);
+                                        m0 + wm * 128, n0 + wn * 128, el);
   };
 
   // One stage (cur holds it, nxt the next one):
