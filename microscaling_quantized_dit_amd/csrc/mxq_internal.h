@@ -156,16 +156,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // GELU, tanh form: 0.5 y (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
-// Since 1 + tanh(u) = 2 / (1 + e^(-2u)), this is y / (1 + 2^(-2u log2 e)): one
-// hardware exp2 and one reciprocal, each within about 1 ulp, with no cancellation
-// for large negative y (the quotient tends to -0) or overflow for large positive
-// y (the exponential tends to 0).
+// Since 1 + tanh(u) = 2 / (1 + e^(-2u)), this is y / (1 + 2^x) with
+// x = -2 log2(e) u = y (c0 + c1 y^2), the constants folded (c0 = -2 log2(e)
+// sqrt(2/pi), c1 = 0.044715 c0): one hardware exp2 and one reciprocal, each within
+// about 1 ulp, five other operations, no cancellation for large negative y (the
+// quotient tends to -0) and no overflow for large positive y (2^x tends to 0).
 __device__ __forceinline__ float gelu_tanh(float y) {
-  const float k0 = 0.7978845608028654f;             // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  const float m2log2e = -2.0f * 1.4426950408889634f; // -2 log2(e)
-  const float u = k0 * (y + k1 * y * y * y);
-  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+  constexpr double kC0 = -2.0 * 1.4426950408889634 * 0.7978845608028654;
+  const float c0 = (float)kC0;
+  const float c1 = (float)(kC0 * 0.044715);
+  const float x = y * __builtin_fmaf(y * y, c1, c0);
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
 }
 
 // s_waitcnt immediate for vmcnt = vm (0..63) and lgkmcnt = lgkm (0..15), expcnt
