@@ -194,6 +194,39 @@ def test_tiled_scales_match_oracle(mxq, shape):
         np.testing.assert_array_equal(_np(s), tile_scales(rs, 8))
 
 
+@pytest.mark.parametrize("layout", ["row", "tiled"])
+@pytest.mark.parametrize("shape", [(64, 128), (192, 640), (320, 1152)])
+def test_writes_stay_in_bounds(mxq, layout, shape):
+    """Codes and scales are written into views of larger buffers filled with a
+    canary byte: everything outside the views keeps it, everything inside is
+    written (the tiled work split has no per-chunk range check)."""
+    import torch
+    R, C = shape
+    x = _dev(inputs.flux_activation(R, C, seed=13, stream="canary"))
+    pad = 4096
+
+    def views(*sizes):
+        bufs = [torch.full((n + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda") for n in sizes]
+        return bufs, [b[pad:pad + n] for b, n in zip(bufs, sizes)]
+
+    bufs, (q, s) = views(R * C, R * C // 32)
+    mxq.quantize_mxfp8(x, out=(q.view(R, C), s.view(R, C // 32)), scale_layout=layout)
+    bufs2, (q2, s2) = views(R * C // 2, R * C // 16)
+    g = torch.empty((1,), dtype=torch.float32, device="cuda")
+    mxq.quantize_nvfp4(x, out=(q2.view(R, C // 2), s2.view(R, C // 16), g), scale_layout=layout)
+    torch.cuda.synchronize()
+    for b in bufs + bufs2:
+        assert (b[:pad] == 0xA5).all().item() and (b[-pad:] == 0xA5).all().item()
+    # the views hold the oracle's values (so every byte was written)
+    bits = inputs.flux_activation(R, C, seed=13, stream="canary")
+    rq, rs = oracle.quantize_mxfp8(bits, oracle.E4M3)
+    np.testing.assert_array_equal(_np(q).reshape(R, C), rq)
+    np.testing.assert_array_equal(_np(s).reshape(R, -1), tile_scales(rs, 4) if layout == "tiled" else rs)
+    rq, rs, _ = oracle.quantize_nvfp4(bits)
+    np.testing.assert_array_equal(_np(q2).reshape(R, -1), rq)
+    np.testing.assert_array_equal(_np(s2).reshape(R, -1), tile_scales(rs, 8) if layout == "tiled" else rs)
+
+
 @pytest.mark.parametrize("rows,cols", [(4608, 12288), (18432, 15360)])
 def test_tiled_scales_full_size(mxq, rows, cols):
     """At the FLUX activation shapes (18432 x 15360 has 17.7 M NVFP4 scales): the
