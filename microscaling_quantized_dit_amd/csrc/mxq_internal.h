@@ -118,9 +118,10 @@ __device__ __forceinline__ void store_nt(uint32_t v, uint32_t* p) { __builtin_no
 // run the byte offset of the scale of row t / 16 + 16 u (P scales per row and step).
 template <int U, int P>
 struct TiledSlab {
-  int64_t chunk0;  // chunk of the thread's first row
-  int64_t scale0;  // scale run offset of the thread's first row
-  int64_t cpr;
+  int64_t chunk0 = 0;  // chunk of the thread's first row
+  int64_t scale0 = 0;  // scale run offset of the thread's first row
+  int64_t cpr = 0;
+  __device__ __forceinline__ TiledSlab() = default;   // row-major scales: unused
   __device__ __forceinline__ TiledSlab(int b, int t, const mxq::ScaleTiling& tl) : cpr(tl.cpr) {
     const int g = b / tl.nst, st = b - g * tl.nst;
     const int64_t row = (int64_t)g * (16 * U) + (t >> 4);

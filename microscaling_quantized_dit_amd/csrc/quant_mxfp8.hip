@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
   constexpr int U = TILED ? kUnrollTiled : kUnroll;
   const int t = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * (kThreads * U);
-  const dev::TiledSlab<U, 4> ts(TILED ? (int)blockIdx.x : 0, t, tiling);
+  const auto ts = TILED ? dev::TiledSlab<U, 4>((int)blockIdx.x, t, tiling) : dev::TiledSlab<U, 4>();
   auto chunk = [&](int u) { return TILED ? ts.chunk(u) : base + u * kThreads + t; };
   uint4 v[U];
 #pragma unroll

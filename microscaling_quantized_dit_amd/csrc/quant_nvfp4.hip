@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   // pass, what it read last is the likeliest to be left in a cache
   const int64_t slab = reverse ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
   const int64_t base = slab * (kThreads * kUnroll);
-  const dev::TiledSlab<kUnroll, 8> ts(TILED ? (int)slab : 0, t, tiling);
+  const auto ts = TILED ? dev::TiledSlab<kUnroll, 8>((int)slab, t, tiling) : dev::TiledSlab<kUnroll, 8>();
   auto chunk = [&](int u) { return TILED ? ts.chunk(u) : base + u * kThreads + t; };
   uint4 v[kUnroll];
 #pragma unroll
