@@ -11,3 +11,10 @@ def tile_scales(s, per_step):
     R, J = s.shape
     return np.ascontiguousarray(
         s.reshape(R // 64, 64, J // per_step, per_step).transpose(0, 2, 1, 3)).reshape(R, J)
+
+
+def untile_scales(t, per_step):
+    """Inverse of tile_scales: tiled-order scales [R, J] -> row-major [R, J]."""
+    R, J = t.shape
+    return np.ascontiguousarray(
+        t.reshape(R // 64, J // per_step, 64, per_step).transpose(0, 2, 1, 3)).reshape(R, J)

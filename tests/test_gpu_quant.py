@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from microscaling_quantized_dit_amd import inputs
-from tests.scale_order import tile_scales
+from tests.scale_order import tile_scales, untile_scales
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +155,26 @@ def test_flux_activation_full_size(mxq, cols):
     rows = np.arange(0, 4608, 7)
     _check_mx(mxq, x, "e5m2", oracle.E5M2, rows=rows)
     _check_nv(mxq, x, rows=rows)
+
+
+@pytest.mark.parametrize("cols", [3072, 15360])
+def test_flux_single_stream_activation_nvfp4(mxq, cols):
+    """The single-stream linears' activations (18432 tokens; 15360 = linear2's
+    input, 566 MB) quantized as the bench step does it: dynamic scale, tiled
+    scales.  The global scale over the whole tensor is bit-exact; codes and scales
+    of 32 rows (first and last included) match the oracle's."""
+    import torch
+    R = 18432
+    x = inputs.flux_activation(R, cols, seed=0, stream="cfg4/x%d" % cols)
+    q, s, g = mxq.quantize_nvfp4(_dev(x), scale_layout="tiled")
+    rg = oracle.nvfp4_global_scale(x)
+    assert np.float32(_np(g)[0]).tobytes() == np.float32(rg).tobytes()
+    rows = np.concatenate([np.arange(0, R - 1, 593), [R - 1]])
+    rq, rs, _ = oracle.quantize_nvfp4(x[rows], global_scale=rg)
+    np.testing.assert_array_equal(_np(q)[rows], rq)
+    np.testing.assert_array_equal(untile_scales(_np(s), 8)[rows], rs)
+    del q, s
+    torch.cuda.empty_cache()
 
 
 def test_deterministic(mxq):
