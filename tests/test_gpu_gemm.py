@@ -318,15 +318,17 @@ def test_flux_single_stream_nvfp4(mxq, name, N, K):
 
 @pytest.mark.parametrize("N", [4096, 16384])
 def test_long_sequence(mxq, N):
-    """M = 32768 tokens, K = 4096, with bias: E4M3, E5M2 and NVFP4; 16 sampled rows."""
+    """M = 32768 tokens, K = 4096, with bias: E4M3, E5M2 and NVFP4; 16 sampled rows.
+    Tiled scales, also required bit-identical to the row-major call."""
     M, K = 32768, 4096
     a = inputs.long_sequence_activation(M, K, seed=0, stream="cfg5/A")
     w = inputs.weight(N, K, seed=0, stream="cfg5/W%d" % N)
     b = inputs.bias(N, K, seed=0, stream="cfg5/b%d" % N)
     rows = _rows(M, 16, 3)
     for fmt in (oracle.E4M3, oracle.E5M2):
-        _assert_close(*run_mx(mxq, MX(a, fmt), MX(w, fmt), bias=b, epi="bias", rows=rows), "cfg5 mx %d" % fmt)
-    _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias", rows=rows), "cfg5 nv")
+        _assert_close(*run_mx(mxq, MX(a, fmt), MX(w, fmt), bias=b, epi="bias", rows=rows, layout="tiled"),
+                      "cfg5 mx %d" % fmt)
+    _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias", rows=rows, layout="tiled"), "cfg5 nv")
 
 
 # ------------------------------------------- split tiles of a partial last round
