@@ -1,0 +1,36 @@
+"""include/mxq.h is a C ABI: a C99 program (tests/c_abi_check.c) compiles against
+it with warnings as errors, links to libmxq.so and gets the documented statuses
+from host-side validation (CPU only: no call reaches a device)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import microscaling_quantized_dit_amd as mxq
+from tests.conftest import ROOT
+
+SUCCESS, INVALID, SHAPE, MISALIGNED, WORKSPACE, DEVICE, LAUNCH = range(7)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_c99_client_compiles_links_and_validates(tmp_path):
+    lib = mxq.library_path()
+    if not os.path.exists(lib):
+        import microscaling_quantized_dit_amd.build as b
+        b.build()
+    libdir = os.path.dirname(lib)
+    exe = tmp_path / "c_abi_check"
+    cmd = ["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c_abi_check.c"), "-o", str(exe), "-L", libdir, "-lmxq",
+           "-Wl,-rpath," + libdir]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    env = dict(os.environ)
+    env["LD_LIBRARY_PATH"] = os.pathsep.join(p for p in ["/opt/rocm/lib", env.get("LD_LIBRARY_PATH", "")] if p)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, env=env, timeout=120).stdout
+    lines = out.split("\n")
+    assert [int(x) for x in lines[:6]] == [INVALID, SHAPE, SHAPE, SHAPE, SHAPE, INVALID]
+    assert int(lines[6]) == 128 * 8 + 384 * 8      # both operands' re-laid scales, no split
+    assert int(lines[7]) == 0                      # cols not a multiple of 16
+    assert "misaligned" in lines[8]
+    assert lines[9] == "1"                         # the last failure left its detail
