@@ -9,6 +9,7 @@ Independent of the C oracle in method, not just in code:
 """
 from __future__ import annotations
 
+import bisect
 from fractions import Fraction as Fr
 
 
@@ -45,6 +46,20 @@ def rne_sat(q: Fr, table) -> int:
         d = abs(q - v)
         if best is None or d < best[0] or (d == best[0] and i % 2 == 0):
             best = (d, i)
+    return best[1]
+
+
+def rne_sat_near(q: Fr, table) -> int:
+    """rne_sat for large inputs: the two table values around q found by bisection,
+    then the same argmin with ties to the even code over those neighbours only.
+    Checked against rne_sat (the full argmin) in the tests."""
+    i = bisect.bisect_right(table, q)        # table[i - 1] <= q < table[i]
+    cands = [j for j in (i - 1, i) if 0 <= j < len(table)]
+    best = None
+    for j in cands:
+        d = abs(q - table[j])
+        if best is None or d < best[0] or (d == best[0] and j % 2 == 0):
+            best = (d, j)
     return best[1]
 
 
@@ -85,7 +100,7 @@ def rn_fp32(v: Fr) -> Fr:
     return r
 
 
-def quant_mx(x_bits, rows: int, cols: int, fmt: int):
+def quant_mx(x_bits, rows: int, cols: int, fmt: int, rnd=rne_sat):
     """MXFP8: per 32-block E = floor(log2 amax) - emax (clamped), codes by argmin."""
     table = TABLES[fmt]
     emax = floor_log2(table[-1])
@@ -99,12 +114,12 @@ def quant_mx(x_bits, rows: int, cols: int, fmt: int):
             E = -127 if amax == 0 else min(127, max(-127, floor_log2(amax) - emax))
             s[r][b] = E + 127
             for i in range(32):
-                code = rne_sat(abs(vals[i]) / Fr(2) ** E, table)
+                code = rnd(abs(vals[i]) / Fr(2) ** E, table)
                 q[r][b * 32 + i] = code | (SIGN_BIT[fmt] if blk[i] & 0x8000 else 0)
     return q, s
 
 
-def quant_nv(x_bits, rows: int, cols: int, global_in=None):
+def quant_nv(x_bits, rows: int, cols: int, global_in=None, rnd=rne_sat):
     """NVFP4: s_g = RN_fp32(amax_t / 2688), S_b = RN_E4M3(amax_b / (6 s_g)),
     q = RN_E2M1(x / (S_b s_g)); returns unpacked nibbles."""
     allv = [bf16_value(x_bits[r][c]) for r in range(rows) for c in range(cols)]
@@ -120,11 +135,11 @@ def quant_nv(x_bits, rows: int, cols: int, global_in=None):
             blk = [x_bits[r][b * 16 + i] for i in range(16)]
             vals = [bf16_value(v) for v in blk]
             amax = max(abs(v) for v in vals)
-            sb = rne_sat(amax / (6 * sg), E4M3)
+            sb = rnd(amax / (6 * sg), E4M3)
             s[r][b] = sb
             S = E4M3[sb]
             for i in range(16):
-                mag = 0 if S == 0 else rne_sat(abs(vals[i]) / (S * sg), E2M1)
+                mag = 0 if S == 0 else rnd(abs(vals[i]) / (S * sg), E2M1)
                 q[r][b * 16 + i] = mag | (0x8 if blk[i] & 0x8000 else 0)
     return q, s, sg
 
