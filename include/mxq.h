@@ -45,8 +45,9 @@
  *
  * Conventions:
  *   - All tensor pointers are DEVICE pointers on the current HIP device, owned
- *     by the caller; the library never allocates or frees.  Base pointers must
- *     be 16-byte aligned.
+ *     by the caller; the library never allocates or frees (its one piece of
+ *     device memory is the 1 KiB static scratch of mxq_quantize_nvfp4_noalloc).
+ *     Base pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = default stream).  Every call is
  *     asynchronous on that stream and never synchronizes; outputs are valid
  *     after the caller synchronizes the stream.
@@ -54,7 +55,8 @@
  *     status and launches nothing.  mxq_last_error() gives the detail.
  *   - Inputs must be finite (NaN/Inf inputs give unspecified codes).
  *   - No exceptions cross the ABI; no global mutable state besides a per-thread
- *     error string and a per-device architecture cache.
+ *     error string, per-device caches (architecture, compute units, the scratch
+ *     address) and that scratch.
  *   - Requires a gfx950 device (MXFP8/NVFP4 scaled MFMA); other devices get
  *     MXQ_ERROR_UNSUPPORTED_DEVICE.
  */
@@ -144,6 +146,29 @@ mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols,
                               const float* global_scale_in, void* q, void* scales,
                               mxq_scale_layout scale_layout, float* global_scale_out,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * NVFP4 quantizer that allocates nothing and takes no workspace -- for callers
+ * that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Arguments, layouts, results and errors: as mxq_quantize_nvfp4 without
+ *   workspace and ws_bytes; the results are bit-identical to it.
+ *   Dynamic mode keeps the amax pass's partial maxima in the library's own
+ *   device scratch: a file-scope array of 256 words (1 KiB) per GPU, held until
+ *   the process ends.  The amax pass never uses more than 256 workgroups, so any
+ *   tensor size fits; a shape that would need more returns MXQ_ERROR_WORKSPACE.
+ *   The scratch needs no clearing (every slot read is written first by the same
+ *   call).  All calls on one GPU share it: calls that overlap in time on one GPU
+ *   (on different streams, or from several host threads without ordering) race
+ *   and may produce a wrong global scale; order them on one stream.
+ *   The scratch address is looked up once per device on the first call made
+ *   with that device current (hipGetSymbolAddress); a failed lookup returns
+ *   MXQ_ERROR_LAUNCH.  No call allocates or frees memory.
+ */
+mxq_status mxq_quantize_nvfp4_noalloc(const void* x, int64_t rows, int64_t cols,
+                                      const float* global_scale_in, void* q, void* scales,
+                                      mxq_scale_layout scale_layout, float* global_scale_out,
+                                      void* stream);
 
 /*
  * Static-scale calibration for NVFP4 activations [P5 step 1 "校准": run a small

@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "load", "MXQError", "E4M3", "E5M2", "EPI_NONE", "EPI_BIAS", "EPI_BIAS_GELU_TANH",
-    "quantize_mxfp8", "quantize_nvfp4", "nvfp4_workspace_size", "nvfp4_calibrate", "quantize_fp8_weight",
+    "quantize_mxfp8", "quantize_nvfp4", "quantize_nvfp4_noalloc", "nvfp4_workspace_size", "nvfp4_calibrate", "quantize_fp8_weight",
     "gemm_mxfp8", "gemm_nvfp4", "gemm_bf16_fp8w",
     "library_path",
 ]
@@ -35,6 +35,7 @@ _lock = threading.Lock()
 _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
+           "mxq_quantize_nvfp4_noalloc",
            "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size",
            "mxq_gemm_nvfp4", "mxq_quantize_fp8_v", "mxq_attention_fp8",
            "mxq_gemm_bf16_fp8w", "mxq_status_string", "mxq_last_error"]
@@ -67,6 +68,7 @@ def load():
         lib.mxq_quantize_nvfp4_workspace_size.argtypes = [i64, i64]
         lib.mxq_quantize_nvfp4_workspace_size.restype = sz
         lib.mxq_quantize_nvfp4.argtypes = [P, i64, i64, P, P, P, i32, P, P, sz, P]
+        lib.mxq_quantize_nvfp4_noalloc.argtypes = [P, i64, i64, P, P, P, i32, P, P]
         lib.mxq_nvfp4_calibrate.argtypes = [P, i64, i64, P, P, sz, P]
         lib.mxq_quantize_fp8_weight.argtypes = [P, i64, i64, P, P, P, P, sz, P]
         lib.mxq_gemm_bf16_fp8w.argtypes = [P, P, P, i64, i64, i64, P, i32, P, P]
@@ -80,7 +82,7 @@ def load():
         lib.mxq_status_string.restype = ctypes.c_char_p
         lib.mxq_last_error.argtypes = []
         lib.mxq_last_error.restype = ctypes.c_char_p
-        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight",
+        for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_quantize_nvfp4_noalloc", "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight",
                   "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w", "mxq_quantize_fp8_v",
                   "mxq_attention_fp8"):
             getattr(lib, f).restype = i32
@@ -174,6 +176,24 @@ def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None, 
     lib = load()
     _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _LAYOUT[scale_layout],
                                   _ptr(g), _ptr(workspace), ws_bytes, _stream(stream)))
+    return q, s, g
+
+
+def quantize_nvfp4_noalloc(x, out, global_scale=None, stream=None, scale_layout="row"):
+    """quantize_nvfp4 through the entry point that allocates nothing and takes no
+    workspace (its dynamic-mode partial maxima live in the library's static device
+    scratch).  out = (q, s, g), allocated by the caller as for quantize_nvfp4."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if global_scale is not None:
+        _need(global_scale, torch.float32, "global_scale", x.device)
+    q, s, g = out
+    lib = load()
+    _check(lib.mxq_quantize_nvfp4_noalloc(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s),
+                                          _LAYOUT[scale_layout], _ptr(g), _stream(stream)))
     return q, s, g
 
 

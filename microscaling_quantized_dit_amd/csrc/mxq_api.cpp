@@ -142,6 +142,36 @@ mxq_status mxq_quantize_nvfp4(const void* x, int64_t rows, int64_t cols, const f
                   "mxq_quantize_nvfp4 launch");
 }
 
+mxq_status mxq_quantize_nvfp4_noalloc(const void* x, int64_t rows, int64_t cols, const float* global_scale_in,
+                                      void* q, void* scales, mxq_scale_layout scale_layout,
+                                      float* global_scale_out, void* stream) {
+  if (!x || !q || !scales || !global_scale_out) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  if (rows <= 0 || cols <= 0) return fail(MXQ_ERROR_INVALID_VALUE, "rows and cols must be positive");
+  if (cols % 16 != 0) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "cols (%lld) must be a multiple of 16", (long long)cols);
+  if (rows > INT64_MAX / cols) return fail(MXQ_ERROR_UNSUPPORTED_SHAPE, "rows * cols overflows");
+  mxq_status l = check_scale_layout(scale_layout, rows, cols);
+  if (l != MXQ_SUCCESS) return l;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
+    return fail(MXQ_ERROR_MISALIGNED, "x, q and scales must be 16-byte aligned");
+  if (((uintptr_t)global_scale_out & 3u) || ((uintptr_t)global_scale_in & 3u))
+    return fail(MXQ_ERROR_MISALIGNED, "global scale pointers must be 4-byte aligned");
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  uint32_t* partials = nullptr;
+  if (!global_scale_in) {
+    int words = 0;
+    hipError_t e = mxq::amax_scratch(&partials, &words);
+    if (e != hipSuccess) return fail(MXQ_ERROR_LAUNCH, "scratch address lookup: %s", hipGetErrorString(e));
+    const int need = mxq::nvfp4_amax_partials(rows * cols);
+    if (need > words)
+      return fail(MXQ_ERROR_WORKSPACE, "tensor needs %d partial maxima, the scratch holds %d", need, words);
+  }
+  const mxq::ScaleTiling tiling = mxq::scale_tiling(scale_layout == MXQ_SCALES_TILED ? cols : 0);
+  return launched(mxq::launch_quantize_nvfp4(x, rows * cols, global_scale_in, q, scales, global_scale_out, partials,
+                                             tiling, (hipStream_t)stream),
+                  "mxq_quantize_nvfp4_noalloc launch");
+}
+
 mxq_status mxq_nvfp4_calibrate(const void* x, int64_t rows, int64_t cols, float* running_scale, void* workspace,
                                size_t ws_bytes, void* stream) {
   if (!x || !running_scale) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");

@@ -25,6 +25,11 @@ hipError_t launch_quantize_mxfp8(const void* x, int64_t n_elems, int kind, void*
 
 // Workgroups (= partial maxima) the NVFP4 amax pass uses for n_elems.
 int nvfp4_amax_partials(int64_t n_elems);
+
+// Device address (for the current device) and size in words of the library's
+// own partial-maxima scratch, a file-scope device array used by the entry point
+// that allocates nothing.  Looked up once per device with hipGetSymbolAddress.
+hipError_t amax_scratch(uint32_t** ptr, int* words);
 hipError_t launch_quantize_nvfp4(const void* x, int64_t n_elems, const float* global_in, void* q,
                                  void* scales, float* global_out, uint32_t* partials,
                                  ScaleTiling tiling, hipStream_t stream);

@@ -31,6 +31,8 @@
 // 5 + 4 + 24 significant bits and is exact in fp64.  The fallback is inlined
 // behind a branch that is almost never taken: as a called function it would give
 // every wave a private stack, which alone cost 40% of the kernel's speed.
+#include <atomic>
+
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -474,6 +476,37 @@ hipError_t launch_nvfp4_calibrate(const void* x, int64_t n_elems, float* running
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_calib_fold, dim3(1), dim3(kThreads), 0, stream, partials, n_partials, running);
   return hipGetLastError();
+}
+
+// Scratch for callers that cannot allocate (mxq_quantize_nvfp4_noalloc): the
+// partial maxima of the amax pass in a file-scope device array, one copy per GPU
+// at its own address.  The amax pass never uses more than kMaxPartials
+// workgroups, so 1 KiB covers a tensor of any size.  Each workgroup of the pass
+// writes its own slot before the encode pass reads it, so nothing needs clearing;
+// calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint32_t scratch[kMaxPartials];
+
+hipError_t amax_scratch(uint32_t** ptr, int* words) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<uintptr_t> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uintptr_t a = addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    // The host-side name `scratch` is not a device address: look it up once per
+    // device, with that device current, and use only the address it returns.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    a = (uintptr_t)p;
+    addr[dev].store(a, std::memory_order_release);
+  }
+  *ptr = (uint32_t*)a;
+  *words = kMaxPartials;
+  return hipSuccess;
 }
 
 int nvfp4_amax_partials(int64_t n_elems) {

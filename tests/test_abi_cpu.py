@@ -101,6 +101,28 @@ def test_quantize_nvfp4_validation(lib):
     assert call(rows=128, cols=64, layout=TILED) == SHAPE
 
 
+def test_quantize_nvfp4_noalloc_validation(lib):
+    """The entry point without a workspace validates like mxq_quantize_nvfp4 (minus
+    the workspace checks): nothing is looked up or launched for an invalid call."""
+    def call(x=FAKE, rows=4, cols=64, gin=None, q=FAKE, s=FAKE2, gout=FAKE, layout=ROW):
+        return lib.mxq_quantize_nvfp4_noalloc(x, rows, cols, gin, q, s, layout, gout, None)
+
+    assert call(x=None) == INVALID
+    assert call(s=None) == INVALID
+    assert call(gout=None) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(cols=24) == SHAPE
+    assert call(rows=1 << 62, cols=64) == SHAPE
+    assert call(q=MIS) == MISALIGNED
+    assert call(gout=FAKE + 2) == MISALIGNED
+    assert call(gin=FAKE + 1) == MISALIGNED
+    assert call(layout=3) == INVALID
+    assert call(layout=TILED) == SHAPE
+    if not gpu_available():
+        assert call() == DEVICE              # valid arguments reach the device check
+        assert call(gin=FAKE) == DEVICE
+
+
 def test_nvfp4_calibrate_validation(lib):
     need = lib.mxq_quantize_nvfp4_workspace_size(4, 64)
 
