@@ -1,13 +1,16 @@
 // FP8 multi-head attention for gfx950 (page "NVIDIA Blackwell平台FP4量化技术解析与图像
 // 生成优化", section 2.1: the mixed-precision configuration runs multi-head
-// attention in FP8).  Per head, with head dimension 128:
-//   S = (s_q s_k / sqrt(128)) Q_c K_c^T          Q_c, K_c: per-tensor E4M3 codes
-//   online softmax over key blocks of 64, in key order: m' = max(m, max_j S_j),
-//   P_j = exp(S_j - m'), l = l e^(m - m') + sum_j P_j,
-//   acc = acc e^(m - m') + sum_j val(RN_E4M3(256 P_j)) V_c[j]
-//   O = s_v acc / (256 l)                       (bf16, one rounding)
-// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit
-// scales): exact products, fp32 accumulation.
+// attention in FP8).  Per head, with head dimension 128, for query row i:
+//   S_j = (s_q s_k / sqrt(128)) Q_c[i] . K_c[j]   Q_c, K_c: per-tensor E4M3 codes
+//   m = max_j S_j (over every key), P_j = exp(S_j - m), l = sum_j P_j,
+//   O[i] = s_v sum_j val(RN_E4M3(256 P_j)) V_c[j] / (256 l)   (bf16, one rounding)
+// i.e. softmax attention whose probabilities enter the second product as E4M3
+// codes of 256 P, quantized against the row's own maximum -- no blocking of the
+// keys is part of the definition.  Two passes over the keys: the first finds the
+// row maximum, the second encodes P and accumulates l and the P.V product with
+// that maximum fixed, so nothing is ever rescaled.  Both products run on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit scales): exact products,
+// fp32 accumulation.
 //
 // Layout.  S is computed transposed, S^T = K Q^T (K the first operand), so that
 // lane l holds query l % 32 and, per 32-key tile t, the 16 keys
@@ -20,9 +23,9 @@
 // query in its accumulators (16 per 32-column tile and lane group).
 //
 // Work: one workgroup of 4 waves per 128 queries of a head (32 queries per wave);
-// K and V blocks of 64 keys go global -> LDS by buffer_load ... lds into two
-// buffers (XOR-swizzled rows: conflict-free reads), the next block landing while
-// the current one is used; Q stays in registers.
+// K (first pass) and K and V (second pass) blocks of 64 keys go global -> LDS by
+// buffer_load ... lds into two buffers (XOR-swizzled rows: conflict-free reads),
+// the next block landing while the current one is used; Q stays in registers.
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -85,12 +88,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
   const int krow = lane >> 3, kcx = (lane & 7) ^ (krow >> 1);
   const int vok0 = krow * kD + kcx * 16, vok1 = krow * kD + (kcx ^ 4) * 16;
   const int vov = (lane >> 2) * L + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
-  auto dma = [&](uint8_t* kb, uint8_t* vb, int blk) {
+  auto dma_k = [&](uint8_t* kb, int blk) {
     const int key0 = blk * kKB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kb + 16 * wave * kD), 16, vok0,
                                              (key0 + 16 * wave) * kD, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kb + (16 * wave + 8) * kD), 16, vok1,
                                              (key0 + 16 * wave + 8) * kD, 0, 0);
+  };
+  auto dma = [&](uint8_t* kb, uint8_t* vb, int blk) {
+    const int key0 = blk * kKB;
+    dma_k(kb, blk);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vb + 32 * wave * kKB), 16, vov,
                                              32 * wave * L + key0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vb + (32 * wave + 16) * kKB), 16, vov,
@@ -119,8 +126,57 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
 
   // scores in the log2 domain: x = S log2(e) = c2 * (sum of code products)
   const float c2 = (*qs) * (*ks) * (0.08838834764831845f * 1.4426950408889634f);
-  // running maximum of x; l_run = 256 * (sum of P) over this lane group's keys
-  float m_run = -__builtin_inff(), l_run = 0.0f;
+
+  // raw score sums of this lane's query against the 64 keys of a K block: two
+  // 32-key tiles, 16 keys per lane group each
+  auto scores = [&](const uint8_t* kb, v16f (&s)[2]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[tt][v] = 0.0f;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) s[tt] = mfma8(kfrag(kb, tt, hd), qf[hd], s[tt]);
+    }
+  };
+
+  // ---- Pass 1: the row maximum over every key, on the raw sums (c2 > 0 keeps the
+  // order and fp32 rounding is monotone, so max_j (c2 s_j) = c2 max_j s_j).
+  // Block b uses buffer b & 1; after it every wave waits for block b + 1 and for
+  // its own LDS reads, and at the barrier buffer b & 1 is free for block b + 2.
+  float mraw = -__builtin_inff();
+  auto max_block = [&](const uint8_t* kb) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {   // one 32-key tile at a time: fewer live registers
+      v16f s1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s1[v] = 0.0f;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) s1 = mfma8(kfrag(kb, tt, hd), qf[hd], s1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, s1[v]);
+    }
+  };
+  dma_k(k0, 0);
+  dma_k(k1, 1);
+  __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
+  __syncthreads();
+  for (int b = 0; b < nkb; b += 2) {
+    max_block(k0);
+    __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    __syncthreads();
+    if (b + 2 < nkb) dma_k(k0, b + 2);
+    max_block(k1);
+    __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    __syncthreads();
+    if (b + 3 < nkb) dma_k(k1, b + 3);
+  }
+  mraw = fmaxf(mraw, __shfl_xor(mraw, 32));   // the query's other 32 keys of each tile
+  // 256 P = 2^(x - m + 8): the scaling, the offset and the factor 256 in one fma
+  const float off = 8.0f - mraw * c2;
+
+  // ---- Pass 2: l_run = 256 * (sum of P) over this lane group's keys, and
+  // acc = sum of val(RN_E4M3(256 P)) V_c over them
+  float l_run = 0.0f;
   v16f acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -129,26 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
 
   auto block = [&](const uint8_t* kb, const uint8_t* vb) {
     v16f s[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[tt][v] = 0.0f;
-#pragma unroll
-      for (int hd = 0; hd < 2; ++hd) s[tt] = mfma8(kfrag(kb, tt, hd), qf[hd], s[tt]);
-    }
-    // block maximum on the raw sums (c2 > 0 keeps the order; rounding is monotone)
-    float mraw = -__builtin_inff();
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mraw = fmaxf(mraw, s[tt][v]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));   // the query's other 32 keys
-    const float m_new = fmaxf(m_run, mraw * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first block
-    m_run = m_new;
-    // 256 P = 2^(x - m + 8), with the scaling, the offset and the factor 256 in one fma
-    const float off = 8.0f - m_new;
-    float psum = 0.0f;
+    scores(kb, s);
     uint32_t pw[8];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -158,26 +195,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_attention_fp8(const uint8_t* __
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][4 * vq + u], c2, off));
-          psum += p[u];
+          l_run += p[u];
         }
         // E4M3 codes of 256 P (at most 256: below E4M3's saturation)
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[4 * tt + vq] = (uint32_t)w;
       }
-    l_run = l_run * alpha + psum;
     const v8i pb = v8i{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[dt][v] *= alpha;
-      acc[dt] = mfma8(vfrag(vb, dt), pb, acc[dt]);
-    }
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = mfma8(vfrag(vb, dt), pb, acc[dt]);
   };
 
-  // Prologue: blocks 0 and 1 in flight, wait for both.  Then block b uses buffer
-  // b & 1; after it every wave waits for block b + 1 and for its own LDS reads, and
-  // at the barrier buffer b & 1 is free for block b + 2.
+  // Same buffer discipline as pass 1 (whose last barrier freed both buffers).
   dma(k0, v0, 0);
   dma(k1, v1, 1);
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);

@@ -288,14 +288,11 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=EPI_NONE, row_idx=No
 #   - Q, K, V each quantized per tensor to E4M3 (the per-tensor quantizer above);
 #   - both products on FP8 operands: S from the Q and K codes, and P V with the
 #     probabilities P encoded as E4M3 codes of P * 256 (P <= 1, so at most 256);
-#   - softmax in the online (running-maximum) form over key blocks of 64 in key
-#     order: for each block, m' = max(m, max S), P = exp(S - m'), the running
-#     normalizer l = l * exp(m - m') + sum P (unquantized P) and the running
-#     numerator acc = acc * exp(m - m') + q(P) V;  O = acc / l.
-# The quantized P depends on the running maximum at its block, which is why the
-# oracle takes the blocked algorithm's steps in order.
+#   - softmax against the row's exact maximum: m = max_j S_j over every key,
+#     P_j = exp(S_j - m), l = sum_j P_j (unquantized), O = sum_j q(P_j) V_j / l.
+# The quantized P depends only on the row's scores, not on any order or blocking
+# of the keys.
 
-ATTN_BLOCK = 64          # keys per online-softmax block
 ATTN_P_SCALE = 256.0     # P is encoded as E4M3 codes of P * 256
 
 
@@ -306,12 +303,30 @@ def attention_p_quantize(p: np.ndarray) -> np.ndarray:
     return (_table("e4m3")[codes] / ATTN_P_SCALE).reshape(p.shape)
 
 
-def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize_p: bool = True,
-                     return_l: bool = False):
-    """Online-softmax attention of fp64 rows q [R, d] over k, v [L, d]:
-    acc / l as above, with scores S = sm_scale * q . k.  quantize_p=False keeps P
-    unquantized (plain softmax attention, computed blockwise).  return_l: also
-    the final normalizer l = sum_j exp(S_j - max S) per row."""
+def attention_rowmax(q, k, v, sm_scale: float, quantize_p: bool = True, return_p: bool = False):
+    """Softmax attention of fp64 rows q [R, d] over k, v [L, d], in the textbook
+    two-pass order: scores S = sm_scale * q . k, the row maximum m over all keys,
+    P = exp(S - m), l = sum P, O = sum q(P) v / l (q(P) = P when quantize_p is
+    False).  return_p: also (P [R, L], l [R])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S = (q @ k.T) * sm_scale
+    m = S.max(axis=1)
+    P = np.exp(S - m[:, None])
+    l = P.sum(axis=1)
+    Pq = attention_p_quantize(P) if quantize_p else P
+    O = (Pq @ v) / l[:, None]
+    return (O, P, l) if return_p else O
+
+
+def attention_online(q, k, v, sm_scale: float, block: int = 64, quantize_p: bool = True):
+    """The single-pass (running maximum) algorithm over key blocks of `block`, in
+    key order: m' = max(m, max S), P = exp(S - m'), l = l e^(m - m') + sum P,
+    acc = acc e^(m - m') + q(P) v, O = acc / l.  Not the definition above (with
+    quantize_p its P is encoded against the running maximum); it equals it when
+    one block holds every key, and without quantization for any block size, which
+    the pins check."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -328,17 +343,18 @@ def attention_online(q, k, v, sm_scale: float, block: int = ATTN_BLOCK, quantize
         Pq = attention_p_quantize(P) if quantize_p else P
         acc = acc * alpha[:, None] + Pq @ v[b0:b0 + block]
         m = m_new
-    return (acc / l[:, None], l) if return_l else acc / l[:, None]
+    return acc / l[:, None]
 
 
 def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: int, row_idx=None,
-                  return_l: bool = False):
+                  return_p: bool = False):
     """FP8 attention, fp64 result [heads, R, d]: codes [heads * L, d] (head h is
     rows h*L .. h*L + L - 1), per-tensor fp32 decode scales, softmax scale
     1/sqrt(d).  Scores are formed as (s_q s_k / sqrt(d)) * sum val(q) val(k) -- the
     code products and their sum are exact in fp64 -- and V enters as its code
     values, with s_v applied to the result.  row_idx: query rows within each head
-    (all when None).  return_l: also the normalizers [heads, R]."""
+    (all when None).  return_p: also the exact probabilities P [heads, R, L] and
+    normalizers l [heads, R] (for the tolerance of a comparison)."""
     e43 = _table("e4m3")
     qv = e43[np.asarray(q_codes, np.uint8)]
     kv = e43[np.asarray(k_codes, np.uint8)]
@@ -347,15 +363,18 @@ def attention_fp8(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, heads: i
     L = n // heads
     sm = float(np.float64(np.float32(q_scale)) * np.float64(np.float32(k_scale))) / np.sqrt(d)
     sv = float(np.float32(v_scale))
-    out, ls = [], []
+    out, ps, ls = [], [], []
     for h in range(heads):
         qh = qv[h * L:(h + 1) * L]
         if row_idx is not None:
             qh = qh[np.asarray(row_idx)]
-        o, l = attention_online(qh, kv[h * L:(h + 1) * L], vv[h * L:(h + 1) * L], sm, return_l=True)
+        o, p, l = attention_rowmax(qh, kv[h * L:(h + 1) * L], vv[h * L:(h + 1) * L], sm, return_p=True)
         out.append(sv * o)
+        ps.append(p)
         ls.append(l)
-    return (np.stack(out), np.stack(ls)) if return_l else np.stack(out)
+    if return_p:
+        return np.stack(out), np.stack(ps), np.stack(ls)
+    return np.stack(out)
 
 
 def max_threads() -> int:

@@ -289,42 +289,52 @@ def test_deterministic(mxq):
 # ------------------------------------------- full FLUX shapes (sampled rows)
 
 def _rows(M, n, seed):
+    """At least n seeded rows spread over every 256-row tile of the output (the
+    same number in each tile, at offsets drawn per tile), plus rows 0 and M - 1."""
     rng = np.random.RandomState(seed)
-    return np.sort(np.concatenate([[0, M - 1], rng.choice(M, n - 2, replace=False)]))
+    tiles = -(-M // 256)
+    per = -(-n // tiles)
+    rows = {0, M - 1}
+    for t in range(tiles):
+        span = min(256, M - 256 * t)
+        rows.update(256 * t + rng.choice(span, min(per, span), replace=False))
+    return np.array(sorted(rows))
 
 
 @pytest.mark.parametrize("name,N,K,epi", [("qkv", 9216, 3072, "none"), ("out", 3072, 3072, "none"),
                                           ("mlp_up", 12288, 3072, "bias_gelu"), ("mlp_down", 3072, 12288, "none")])
 def test_flux_double_stream_mxfp8(mxq, name, N, K, epi):
-    """FLUX double-stream linears at M = 4608 tokens, MXFP8 E4M3; 64 sampled rows.
+    """FLUX double-stream linears at M = 4608 tokens, MXFP8 E4M3; 256 sampled rows
+    spread over every 256-row tile.
     Tiled scales, as the bench step runs them (and row-major, bit-identical)."""
     M = 4608
     A = MX(inputs.flux_activation(M, K, seed=0, stream="cfg3/%s/A" % name), oracle.E4M3)
     W = MX(inputs.weight(N, K, seed=0, stream="cfg3/%s/W" % name), oracle.E4M3)
     b = inputs.bias(N, K, seed=0, stream="cfg3/%s/b" % name) if epi != "none" else None
-    _assert_close(*run_mx(mxq, A, W, bias=b, epi=epi, rows=_rows(M, 64, 1), layout="tiled"), name)
+    _assert_close(*run_mx(mxq, A, W, bias=b, epi=epi, rows=_rows(M, 256, 1), layout="tiled"), name)
 
 
 @pytest.mark.parametrize("name,N,K", [("linear1", 21504, 3072), ("linear2", 3072, 15360)])
 def test_flux_single_stream_nvfp4(mxq, name, N, K):
     """FLUX single-stream linears at batch 4 (M = 18432), NVFP4 with a dynamic
-    activation scale; 32 sampled rows.  Tiled scales and a workspace (linear2's
+    activation scale; 256 sampled rows over every 256-row tile.  Tiled scales and a workspace (linear2's
     partial last round split along K), as the bench step runs them."""
     M = 18432
     A = NV(inputs.flux_activation(M, K, seed=0, stream="cfg4/%s/A" % name))
     W = NV(inputs.weight(N, K, seed=0, stream="cfg4/%s/W" % name))
-    _assert_close(*run_nv(mxq, A, W, rows=_rows(M, 32, 2), layout="tiled"), name)
+    _assert_close(*run_nv(mxq, A, W, rows=_rows(M, 256, 2), layout="tiled"), name)
 
 
 @pytest.mark.parametrize("N", [4096, 16384])
 def test_long_sequence(mxq, N):
-    """M = 32768 tokens, K = 4096, with bias: E4M3, E5M2 and NVFP4; 16 sampled rows.
+    """M = 32768 tokens, K = 4096, with bias: E4M3, E5M2 and NVFP4 on operands the
+    oracle quantized; 256 sampled rows, two in every 256-row tile.
     Tiled scales, also required bit-identical to the row-major call."""
     M, K = 32768, 4096
     a = inputs.long_sequence_activation(M, K, seed=0, stream="cfg5/A")
     w = inputs.weight(N, K, seed=0, stream="cfg5/W%d" % N)
     b = inputs.bias(N, K, seed=0, stream="cfg5/b%d" % N)
-    rows = _rows(M, 16, 3)
+    rows = _rows(M, 256, 3)
     for fmt in (oracle.E4M3, oracle.E5M2):
         _assert_close(*run_mx(mxq, MX(a, fmt), MX(w, fmt), bias=b, epi="bias", rows=rows, layout="tiled"),
                       "cfg5 mx %d" % fmt)

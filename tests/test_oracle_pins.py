@@ -460,15 +460,29 @@ def _softmax_attention_two_pass(q, k, v, sm):
 
 
 def test_attention_online_equals_two_pass():
-    """Without P quantization the blocked running-maximum algorithm is plain
-    softmax attention: any block size, including 1 and the whole key range, gives
-    the two-pass result (a missing rescale or a stale maximum would not)."""
+    """Without P quantization the oracle's attention is plain softmax attention,
+    and so is the blocked running-maximum algorithm for any block size, including 1
+    and the whole key range (a missing rescale or a stale maximum would not be)."""
     rng = np.random.RandomState(5)
     q, k, v = rng.randn(7, 16) * 2, rng.randn(200, 16) * 2, rng.randn(200, 16)
     ref = _softmax_attention_two_pass(q, k, v, 0.37)
+    np.testing.assert_allclose(oracle.attention_rowmax(q, k, v, 0.37, quantize_p=False), ref, rtol=1e-12, atol=1e-14)
     for block in (1, 7, 64, 200):
         got = oracle.attention_online(q, k, v, 0.37, block=block, quantize_p=False)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_quantized_p_independent_of_blocking():
+    """With P quantized, the definition (P against the exact row maximum) is what
+    the running-maximum algorithm computes when one block holds every key; with
+    smaller blocks the keys before the last maximum move are encoded against a
+    lower maximum, so the results differ (the reason the definition is two-pass)."""
+    rng = np.random.RandomState(15)
+    q, k, v = rng.randn(6, 16), rng.randn(256, 16), rng.randn(256, 16)
+    ref = oracle.attention_rowmax(q, k, v, 0.5)
+    np.testing.assert_allclose(oracle.attention_online(q, k, v, 0.5, block=256), ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.attention_online(q, k, v, 0.5, block=1000), ref, rtol=1e-13, atol=1e-15)
+    assert np.abs(oracle.attention_online(q, k, v, 0.5, block=16) - ref).max() > 1e-6
 
 
 def test_attention_p_quantizer_worked_values():
@@ -487,7 +501,7 @@ def test_attention_equal_scores_give_the_mean():
     q = rng.randn(5, 8)
     k = np.tile(rng.randn(1, 8), (130, 1))
     v = rng.randn(130, 8)
-    got = oracle.attention_online(q, k, v, 0.5)
+    got = oracle.attention_rowmax(q, k, v, 0.5)
     np.testing.assert_allclose(got, np.tile(v.mean(axis=0), (5, 1)), rtol=1e-14, atol=1e-15)
 
 
@@ -501,7 +515,7 @@ def test_attention_dominant_key_selects_its_row():
     k = np.zeros((150, d))
     k[97, 0] = 40.0
     v = np.random.RandomState(7).randn(150, d)
-    got = oracle.attention_online(q, k, v, 1.0)
+    got = oracle.attention_rowmax(q, k, v, 1.0)
     np.testing.assert_allclose(got[0], v[97], rtol=1e-15, atol=1e-15)
 
 
@@ -511,14 +525,14 @@ def test_attention_quantized_error_bound():
     rng = np.random.RandomState(8)
     q, k, v = rng.randn(9, 32), rng.randn(256, 32), rng.randn(256, 32)
     exact = _softmax_attention_two_pass(q, k, v, 0.2)
-    quant = oracle.attention_online(q, k, v, 0.2)
+    quant = oracle.attention_rowmax(q, k, v, 0.2)
     assert np.abs(quant - exact).max() <= (2.0 ** -4 + 2.0 ** -18 * 256) * np.abs(v).max()
     assert np.abs(quant - exact).max() > 0          # the quantization is really applied
 
 
 def test_attention_fp8_codes_and_scales():
     """attention_fp8 forms scores from the code values with s_q s_k / sqrt(d) and
-    applies s_v to the result: the same as attention_online on dequantized
+    applies s_v to the result: the same as attention_rowmax on dequantized
     operands."""
     rng = np.random.RandomState(9)
     heads, L, d = 2, 96, 16
@@ -528,6 +542,6 @@ def test_attention_fp8_codes_and_scales():
     got = oracle.attention_fp8(qc, qs, kc, ks, vc, vs, heads)
     for h in range(heads):
         sl = slice(h * L, (h + 1) * L)
-        ref = oracle.attention_online(e43[qc[sl]] * float(qs), e43[kc[sl]] * float(ks), e43[vc[sl]] * float(vs),
+        ref = oracle.attention_rowmax(e43[qc[sl]] * float(qs), e43[kc[sl]] * float(ks), e43[vc[sl]] * float(vs),
                                       1.0 / np.sqrt(d))
         np.testing.assert_allclose(got[h], ref, rtol=1e-12, atol=1e-14)
