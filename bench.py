@@ -236,6 +236,20 @@ class Workload:
             return "k_quant_mxfp8<0, %s>" % TILED_NAME
         return "k_amax_partials + k_quant_nvfp4<%s>" % TILED_NAME
 
+    def single_launch(self, mxq, name):
+        """Does this op run as one kernel launch?  The MXFP8 GEMMs do; an NVFP4 GEMM
+        does unless its workspace holds split tiles (its size beyond the two
+        operands' re-laid scales, which the tiled order leaves unused), and the
+        dynamic NVFP4 quantizer is two launches (amax, encode)."""
+        if name.startswith("quant_nvfp4"):
+            return False
+        if name.startswith("gemm_nvfp4"):
+            L = next(L for L in self.nv if "gemm_nvfp4_" + L["name"] == name)
+            r256 = lambda b: (b + 255) // 256 * 256
+            scales = r256(M_NV * L["K"] // 16) + r256(L["N"] * L["K"] // 16)
+            return mxq.gemm_nvfp4_workspace_size(M_NV, L["N"], L["K"]) <= scales
+        return True
+
     def ops(self, mxq):
         """(op name, kind, callable) in step order."""
         out = []
@@ -347,12 +361,16 @@ def weight_only_fp8_variant(torch, mxq, inputs, wl, reps: int = 20):
         wq, ws = mxq.quantize_fp8_weight(w)
         c = torch.empty((M_MX, L["N"]), dtype=torch.bfloat16, device="cuda")
         g_ms = timed(lambda: mxq.gemm_bf16_fp8w(L["x"], wq, ws, bias=L["b"], epi=L["epi"], out=c))
-        t_ms = timed(lambda: torch.matmul(L["x"], w.t()))
+        if L["epi"] == "bias_gelu":   # torch's bf16 GEMM with the same epilogue
+            t_ms = timed(lambda: torch.nn.functional.gelu(torch.addmm(L["b"], L["x"], w.t()), approximate="tanh"))
+        else:
+            t_ms = timed(lambda: torch.matmul(L["x"], w.t()))
         flops = 2 * M_MX * L["N"] * L["K"]
         rate = flops / (g_ms * 1e-3) / 1e12
         out["gemm_bf16_fp8w_" + L["name"]] = {
             "shape": [M_MX, L["N"], L["K"]], "epi": L["epi"], "ms": round(g_ms, 4), "TFLOP/s": round(rate, 1),
             "frac": round(rate / PEAK_BF16_TFLOPS, 4), "torch_bf16_ms": round(t_ms, 4),
+            "vs_torch_bf16": round(g_ms / t_ms, 4),
             "quantize_weight_ms": round(q_ms, 4)}
         del w, wq, ws, c
     return out
@@ -392,6 +410,160 @@ def fp8_attention_variant(torch, mxq, inputs, reps: int = 20):
     return {"shape": {"heads": heads, "tokens": L, "head_dim": d}, "flops": flops, "ms": round(a_ms, 4),
             "TFLOP/s": round(rate, 1), "frac_of_fp8_peak": round(rate / PEAK_TFLOPS["fp8"], 4),
             "quantize_qkv_ms": round(q_ms, 4), "torch_bf16_sdpa_ms": round(t_ms, 4)}
+
+
+def measured_peaks(torch):
+    """What this machine attains, measured in the same run (libmxq_probes.so): the
+    scaled fp8 and the fp16 matrix-core rates on back-to-back MFMAs from every
+    compute unit with random register data, with the shader clock observed under
+    that load, and a streaming 1 GiB device copy (bytes read + written)."""
+    from microscaling_quantized_dit_amd import probes
+    fp8, clk8 = probes.mfma_rate("fp8")
+    fp16, clk16 = probes.mfma_rate("fp16")
+    copy = probes.hbm_copy(1 << 30)
+    return {"mfma_fp8_TFLOP/s": round(fp8, 1), "sclk_MHz_under_fp8": round(clk8, 0),
+            "mfma_fp16_TFLOP/s": round(fp16, 1), "sclk_MHz_under_fp16": round(clk16, 0),
+            "hbm_copy_GB/s": round(copy, 1),
+            "note": "random register data; spec peaks: fp8 5000, fp16 2500 TFLOP/s at 2.4 GHz, HBM 8000 GB/s"}
+
+
+def _graph_time(torch, fn, reps):
+    """Mean ms of one replay of fn() captured as a HIP graph (replayed `reps` times
+    back to back after one warm replay), timed with events on the replay stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                          # the calls once outside the graph (allocator warm-up)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def quantizer_only(torch, mxq, inputs, copy_gbps, reps: int = 10):
+    """The quantizer-only workload: bf16 activations [4608, 3072] and [4608, 12288]
+    (FLUX recipe), MXFP8 E4M3 (and E5M2) and NVFP4 with a dynamic scale, block
+    scales in the GEMM-tiled order.  Cold: launches rotate over copies of the
+    tensor and their outputs totalling >= 1 GiB (more than the 256 MB last-level
+    cache), so every input comes from HBM.  Warm: one copy launched repeatedly.
+    All launches of a pass are one captured graph (no host gaps)."""
+    out = {"recipe": "flux_activation seed 0; cold = rotating copies totalling >= 1 GiB; warm = one copy",
+           "nvfp4_two_read_bound_frac": round(2.5625 / 4.5625, 4)}
+    for rows, cols in ((4608, 3072), (4608, 12288)):
+        x0 = inputs.to_torch(inputs.flux_activation(rows, cols, seed=0, stream="cfg2/%dx%d" % (rows, cols)), "cuda")
+        n = rows * cols
+        for fmt in ("mxfp8_e4m3", "mxfp8_e5m2", "nvfp4"):
+            if fmt == "nvfp4":
+                per_set = 2 * n + n // 2 + n // 16
+                algo = 2 * n + n // 2 + n // 16 + 4
+            else:
+                per_set = 2 * n + n + n // 32
+                algo = per_set
+            sets = max(2, -(-(1 << 30) // per_set))
+            xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+            if fmt == "nvfp4":
+                outs = [(torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                         torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda"),
+                         torch.empty((1,), dtype=torch.float32, device="cuda")) for _ in range(sets)]
+                ws = torch.empty((max(mxq.nvfp4_workspace_size(rows, cols), 4),), dtype=torch.uint8, device="cuda")
+
+                def one(i):
+                    mxq.quantize_nvfp4(xs[i], out=outs[i], workspace=ws, scale_layout=SCALES)
+            else:
+                kind = fmt.split("_")[1]
+                outs = [(torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
+                         torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+
+                def one(i, kind=kind):
+                    mxq.quantize_mxfp8(xs[i], kind, out=outs[i], scale_layout=SCALES)
+
+            cold = _graph_time(torch, lambda: [one(i) for i in range(sets)], reps) / sets
+            warm = _graph_time(torch, lambda: [one(0) for _ in range(sets)], reps) / sets
+            rec = {}
+            for tag, ms in (("cold", cold), ("warm", warm)):
+                gbps = algo / (ms * 1e-3) / 1e9
+                rec[tag] = {"ms": round(ms, 4), "GB/s": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                            "frac_of_measured_copy": round(gbps / copy_gbps, 4) if copy_gbps else None}
+                if fmt == "nvfp4":
+                    rec[tag]["frac_of_two_read_bound"] = round(gbps / (PEAK_HBM_GBPS * 2.5625 / 4.5625), 4)
+            rec["buffer_sets"] = sets
+            rec["algorithmic_bytes"] = algo
+            out["%s_%dx%d" % (fmt, rows, cols)] = rec
+            del xs, outs
+        del x0
+    torch.cuda.synchronize()
+    return out
+
+
+def chain_long_sequence(torch, mxq, inputs, reps: int = 5):
+    """The long-sequence chain: bf16 activations [32768, 4096] (N(0, 1), 0.1%
+    outliers x50) quantized per call (tiled scales), then the block-scaled GEMM
+    with bias against a weight [N, 4096] quantized beforehand, N in {4096, 16384},
+    MXFP8 E4M3, MXFP8 E5M2 and NVFP4 (dynamic activation scale).  Each stage and the
+    chain are timed as captured graphs."""
+    M, K = 32768, 4096
+    x = inputs.to_torch(inputs.long_sequence_activation(M, K, seed=0, stream="cfg5/A"), "cuda")
+    out = {"shape": {"M": M, "K": K}, "recipe": "long_sequence_activation seed 0; weights N(0, 1/sqrt(K)); bias"}
+    for N in (4096, 16384):
+        w = inputs.to_torch(inputs.weight(N, K, seed=0, stream="cfg5/W%d" % N), "cuda")
+        b = inputs.to_torch(inputs.bias(N, K, seed=0, stream="cfg5/b%d" % N), "cuda")
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        flops = 2 * M * N * K
+        for fmt in ("e4m3", "e5m2", "nvfp4"):
+            if fmt == "nvfp4":
+                wq, ws_, wg = mxq.quantize_nvfp4(w, scale_layout=SCALES)
+                aq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+                as_ = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
+                ag = torch.empty((1,), dtype=torch.float32, device="cuda")
+                qws = torch.empty((max(mxq.nvfp4_workspace_size(M, K), 4),), dtype=torch.uint8, device="cuda")
+                gsz = mxq.gemm_nvfp4_workspace_size(M, N, K)
+                gws = torch.empty((gsz,), dtype=torch.uint8, device="cuda") if gsz else None
+                qbytes = 2 * M * K + M * K // 2 + M * K // 16 + 4
+
+                def quant():
+                    mxq.quantize_nvfp4(x, out=(aq, as_, ag), workspace=qws, scale_layout=SCALES)
+
+                def gemm():
+                    mxq.gemm_nvfp4(aq, as_, ag, wq, ws_, wg, bias=b, epi="bias", out=c, workspace=gws,
+                                   scale_layout=SCALES)
+                peak = PEAK_TFLOPS["fp4"]
+            else:
+                wq, ws_ = mxq.quantize_mxfp8(w, fmt, scale_layout=SCALES)
+                aq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+                as_ = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+                qbytes = 2 * M * K + M * K + M * K // 32
+
+                def quant(fmt=fmt):
+                    mxq.quantize_mxfp8(x, fmt, out=(aq, as_), scale_layout=SCALES)
+
+                def gemm(fmt=fmt):
+                    mxq.gemm_mxfp8(aq, as_, wq, ws_, bias=b, epi="bias", a_kind=fmt, w_kind=fmt, out=c,
+                                   scale_layout=SCALES)
+                peak = PEAK_TFLOPS["fp8"]
+            q_ms = _graph_time(torch, quant, reps)
+            g_ms = _graph_time(torch, gemm, reps)
+            t_ms = _graph_time(torch, lambda: (quant(), gemm()), reps)
+            gemm_rate = flops / (g_ms * 1e-3) / 1e12
+            out["%s_N%d" % (fmt, N)] = {
+                "quantize_ms": round(q_ms, 4), "quantize_GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+                "gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(gemm_rate, 1),
+                "gemm_frac_of_peak": round(gemm_rate / peak, 4), "peak_TFLOP/s": peak,
+                "chain_ms": round(t_ms, 4), "chain_TFLOP/s": round(flops / (t_ms * 1e-3) / 1e12, 1)}
+        del w, b, c
+    del x
+    torch.cuda.synchronize()
+    return out
 
 
 def cpu_baseline(rows_per_linear: int):
@@ -539,23 +711,33 @@ def main():
     g_ms = sum(per_op[n]["ms"] for n in per_op if n.startswith("gemm"))
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the HIP kernel function with the largest share of the step,
-    # over all its launches (per launch: mean algorithmic work / mean duration)
+    # dominant kernel: the HIP kernel function with the largest share of the step.
+    # Its per-launch figures (mean algorithmic work / mean duration) are taken over
+    # the ops that consist of that one launch (HIP events around the op time exactly
+    # that kernel); an op that adds launches (an NVFP4 GEMM whose partial last round
+    # is split along K adds the split launch and a fixup) is left out of the mean.
     epis = {("gemm_mxfp8_" + L["name"]): L["epi"] for L in wl.mx}
     epis.update({("gemm_nvfp4_" + L["name"]): L["epi"] for L in wl.nv})
     by_kernel = {}
     for name in per_op:
         k = wl.kernel_of(name, epis.get(name, "none"))
         per_op[name]["kernel"] = k
-        d = by_kernel.setdefault(k, {"ms": 0.0, "amount": 0, "launches": 0, "unit": work[name][0], "ops": []})
+        single = wl.single_launch(mxq, name)
+        per_op[name]["single_launch"] = single
+        d = by_kernel.setdefault(k, {"ms": 0.0, "ms1": 0.0, "amount1": 0, "launches1": 0, "unit": work[name][0],
+                                     "ops": [], "excluded": []})
         d["ms"] += per_op[name]["ms"]
-        d["amount"] += work[name][1]
-        d["launches"] += 1
-        d["ops"].append(name)
+        if single:
+            d["ms1"] += per_op[name]["ms"]
+            d["amount1"] += work[name][1]
+            d["launches1"] += 1
+            d["ops"].append(name)
+        else:
+            d["excluded"].append(name)
     dom = max(by_kernel, key=lambda k: by_kernel[k]["ms"])
     d = by_kernel[dom]
-    avg_ms = d["ms"] / d["launches"]
-    per_launch = d["amount"] / d["launches"]
+    avg_ms = d["ms1"] / d["launches1"]
+    per_launch = d["amount1"] / d["launches1"]
     if d["unit"] == "flops":
         peak = PEAK_TFLOPS["fp8"] if "mxfp8" in dom else PEAK_TFLOPS["fp4"]
         achieved = per_launch / (avg_ms * 1e-3) / 1e12
@@ -570,9 +752,9 @@ def main():
         roofline["traffic"] = rec["bytes_per_launch"]
         roofline["traffic_read"] = rec["read_bytes_per_launch"]
         roofline["traffic_write"] = rec["write_bytes_per_launch"]
-    roofline.update({"kernel": dom, "launches_per_step": d["launches"], "ops": d["ops"],
-                     "avg_launch_ms": round(avg_ms, 4), "work_per_launch": per_launch,
-                     "work_unit": d["unit"]})
+    roofline.update({"kernel": dom, "launches_per_step": d["launches1"] + len(d["excluded"]), "ops": d["ops"],
+                     "ops_left_out": d["excluded"], "avg_launch_ms": round(avg_ms, 4),
+                     "work_per_launch": per_launch, "work_unit": d["unit"]})
     if "nvfp4" in dom:
         roofline["frac_of_fp16_mfma_peak"] = round(achieved / PEAK_TFLOPS["fp16"], 4)
 
@@ -606,6 +788,20 @@ def main():
         "ops": per_op,
         "roofline": roofline,
     }
+    print("bench: measured peaks", file=sys.stderr, flush=True)
+    peaks = measured_peaks(torch)
+    result["measured_peaks"] = peaks
+    if roofline["bound"] == "mfma":
+        # the MXFP8 GEMM runs on the scaled fp8 matrix core, the NVFP4 GEMM's exact
+        # scheme on the fp16 one
+        mp = peaks["mfma_fp8_TFLOP/s"] if "mxfp8" in dom else peaks["mfma_fp16_TFLOP/s"]
+    else:
+        mp = peaks["hbm_copy_GB/s"]
+    roofline["peak_measured"] = mp
+    roofline["frac_measured"] = round(achieved / mp, 4)
+    print("bench: quantizer-only and long-sequence chain legs", file=sys.stderr, flush=True)
+    result["quantizer_only"] = quantizer_only(torch, mxq, inputs, peaks["hbm_copy_GB/s"])
+    result["long_sequence_chain"] = chain_long_sequence(torch, mxq, inputs)
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
     result["fp8_attention"] = fp8_attention_variant(torch, mxq, inputs)

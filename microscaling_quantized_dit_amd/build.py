@@ -1,4 +1,5 @@
-"""Build libmxq.so (the gfx950 HIP kernels + C-ABI host layer) in-tree with hipcc.
+"""Build libmxq.so (the gfx950 HIP kernels + C-ABI host layer) in-tree with hipcc,
+and libmxq_probes.so (measurement probes for the bench and the tests).
 
     python -m microscaling_quantized_dit_amd.build
 
@@ -16,6 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxq.so")
+PROBES_LIB = os.path.join(PKG, "libmxq_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 SOURCES = ["quant_mxfp8.hip", "quant_nvfp4.hip", "gemm_mxfp8.hip", "gemm_nvfp4.hip", "gemm_w8.hip", "gemm_fixup.hip",
            "attention_fp8.hip", "mxq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -37,14 +40,15 @@ def build(verbose: bool = False) -> str:
         subprocess.run(cmd, check=True)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(len(SOURCES) + len(PROBES_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBES_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBES_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + lib_objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
