@@ -566,6 +566,40 @@ def chain_long_sequence(torch, mxq, inputs, reps: int = 5):
     return out
 
 
+def fusion_lower_bound(torch, mxq, inputs, wl, reps: int = 20):
+    """Would fusing the activation quantizer into the MXFP8 GEMM's prologue pay on
+    the double-stream linears?  A fused kernel reads the bf16 activation (twice the
+    bytes of its codes) for every output tile column and quantizes it there.  A
+    lower bound of its time: the GEMM with every A stage DMA'd twice and no
+    quantization work at all (libmxq_probes.so).  Each sequence is one captured
+    graph replayed back to back (graph launch latency, alike in all, hides behind
+    the GEMM); fusion can save at most  separate - lower_bound, before paying for
+    quantizing each A tile once per output tile column and for an A stage twice
+    the size in LDS."""
+    from microscaling_quantized_dit_amd import probes
+    out = {"probe": "k_gemm_mxfp8 with each A stage DMA'd twice (same bytes, same place)"}
+    for L in wl.mx:
+        c = torch.empty((M_MX, L["N"]), dtype=torch.bfloat16, device="cuda")
+
+        def quant():
+            mxq.quantize_mxfp8(L["x"], "e4m3", out=(L["aq"], L["as_"]), scale_layout=SCALES)
+
+        def gemm():
+            mxq.gemm_mxfp8(L["aq"], L["as_"], L["wq"], L["ws"], out=c, scale_layout=SCALES)
+
+        def gemm2():
+            probes.gemm_mxfp8_a_twice(L["aq"], L["as_"], L["wq"], L["ws"], c)
+
+        sep = _graph_time(torch, lambda: (quant(), gemm()), reps)
+        g_ms = _graph_time(torch, gemm, reps)
+        lb = _graph_time(torch, gemm2, reps)
+        out[L["name"]] = {"separate_quantize_then_gemm_ms": round(sep, 4), "gemm_ms": round(g_ms, 4),
+                          "fused_lower_bound_ms": round(lb, 4), "fusion_saves_at_most_ms": round(sep - lb, 4),
+                          "fusion_saves_at_most_frac": round((sep - lb) / sep, 4)}
+        del c
+    return out
+
+
 def cpu_baseline(rows_per_linear: int):
     """The oracle (as it is) on a bounded sample: `rows_per_linear` activation rows of
     every linear of the step, quantized (dynamic scales over the sampled rows) and
@@ -802,6 +836,7 @@ def main():
     print("bench: quantizer-only and long-sequence chain legs", file=sys.stderr, flush=True)
     result["quantizer_only"] = quantizer_only(torch, mxq, inputs, peaks["hbm_copy_GB/s"])
     result["long_sequence_chain"] = chain_long_sequence(torch, mxq, inputs)
+    result["fusion_lower_bound"] = fusion_lower_bound(torch, mxq, inputs, wl)
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
     result["fp8_attention"] = fp8_attention_variant(torch, mxq, inputs)

@@ -12,6 +12,7 @@ is no CPU fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -112,18 +113,70 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _need(t, dtype, name, device=None):
+def _on(stream):
+    """Context for a call's allocations and launch: the given stream, so that every
+    tensor the binding allocates (outputs and temporaries) belongs to the stream
+    its kernels run on and the caching allocator cannot hand its memory to another
+    stream while they run; the current stream when none is given."""
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _need(t, dtype, name, device=None, shape=None):
+    """Check a tensor argument on the host, before any launch: type, dtype, shape
+    (when given), then GPU residency, contiguity and device."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if not t.is_cuda:
         raise ValueError("%s must be on a GPU" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if device is not None and t.device != device:
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _outputs(out, specs, device):
+    """Given outputs (checked against specs = [(name, dtype, shape)]) or new ones."""
+    torch = _torch()
+    if out is None:
+        return tuple(torch.empty(shape, dtype=dtype, device=device) for _, dtype, shape in specs)
+    out = tuple(out) if isinstance(out, (tuple, list)) else (out,)
+    if len(out) != len(specs):
+        raise ValueError("out must hold %d tensors" % len(specs))
+    for t, (name, dtype, shape) in zip(out, specs):
+        _need(t, dtype, name, device, shape)
+    return out
+
+
+def _bias(bias, N, device):
+    if bias is not None:
+        torch = _torch()
+        _need(bias, torch.bfloat16, "bias", device)
+        if bias.numel() != N:
+            raise ValueError("bias has %d elements, expected N = %d" % (bias.numel(), N))
+
+
+def _workspace(workspace, device):
+    if workspace is not None:
+        torch = _torch()
+        _need(workspace, torch.uint8, "workspace", device)
+        return workspace.numel()
+    return 0
+
+
+def _x2d(x, name="x"):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    _need(x, torch.bfloat16, name)
+    return x.shape
 
 
 # ------------------------------------------------------------------ quantizers
@@ -133,16 +186,12 @@ def quantize_mxfp8(x, kind="e4m3", out=None, stream=None, scale_layout="row"):
     scales' bytes are in row-major order ("row") or in the GEMM-tiled order
     ("tiled", R % 64 == 0 and C % 128 == 0; the tensor keeps the shape [R, C/32])."""
     torch = _torch()
-    _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
-    R, C = x.shape
-    q, s = out if out is not None else (
-        torch.empty((R, C), dtype=torch.uint8, device=x.device),
-        torch.empty((R, C // 32), dtype=torch.uint8, device=x.device))
+    R, C = _x2d(x)
     lib = load()
-    _check(lib.mxq_quantize_mxfp8(_ptr(x), R, C, _KIND[kind], _ptr(q), _ptr(s), _LAYOUT[scale_layout],
-                                  _stream(stream)))
+    with _on(stream):
+        q, s = _outputs(out, [("q", torch.uint8, (R, C)), ("scales", torch.uint8, (R, C // 32))], x.device)
+        _check(lib.mxq_quantize_mxfp8(_ptr(x), R, C, _KIND[kind], _ptr(q), _ptr(s), _LAYOUT[scale_layout],
+                                      _stream(stream)))
     return q, s
 
 
@@ -150,32 +199,29 @@ def nvfp4_workspace_size(rows: int, cols: int) -> int:
     return int(load().mxq_quantize_nvfp4_workspace_size(rows, cols))
 
 
+def _nvfp4_out_specs(R, C):
+    torch = _torch()
+    return [("q", torch.uint8, (R, C // 2)), ("scales", torch.uint8, (R, C // 16)),
+            ("global_scale_out", torch.float32, (1,))]
+
+
 def quantize_nvfp4(x, global_scale=None, out=None, workspace=None, stream=None, scale_layout="row"):
     """bf16 [R, C] -> (packed E2M1 uint8 [R, C/2], E4M3 uint8 [R, C/16], fp32 [1]
     decode scale).  global_scale: None (dynamic, from amax(x)) or a 1-element fp32
     CUDA tensor (static).  scale_layout as for quantize_mxfp8."""
     torch = _torch()
-    _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
-    R, C = x.shape
+    R, C = _x2d(x)
     if global_scale is not None:
-        _need(global_scale, torch.float32, "global_scale", x.device)
-    if out is not None:
-        q, s, g = out
-    else:
-        q = torch.empty((R, C // 2), dtype=torch.uint8, device=x.device)
-        s = torch.empty((R, C // 16), dtype=torch.uint8, device=x.device)
-        g = torch.empty((1,), dtype=torch.float32, device=x.device)
-    ws_bytes = 0
-    if global_scale is None:
-        ws_bytes = nvfp4_workspace_size(R, C)
-        if workspace is None:
-            workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=x.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+        _need(global_scale, torch.float32, "global_scale", x.device, (1,))
+    ws_bytes = _workspace(workspace, x.device)
     lib = load()
-    _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _LAYOUT[scale_layout],
-                                  _ptr(g), _ptr(workspace), ws_bytes, _stream(stream)))
+    with _on(stream):
+        q, s, g = _outputs(out, _nvfp4_out_specs(R, C), x.device)
+        if global_scale is None and workspace is None:
+            ws_bytes = max(nvfp4_workspace_size(R, C), 4)
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+        _check(lib.mxq_quantize_nvfp4(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s), _LAYOUT[scale_layout],
+                                      _ptr(g), _ptr(workspace), ws_bytes, _stream(stream)))
     return q, s, g
 
 
@@ -184,13 +230,12 @@ def quantize_nvfp4_noalloc(x, out, global_scale=None, stream=None, scale_layout=
     workspace (its dynamic-mode partial maxima live in the library's static device
     scratch).  out = (q, s, g), allocated by the caller as for quantize_nvfp4."""
     torch = _torch()
-    _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
-    R, C = x.shape
+    R, C = _x2d(x)
     if global_scale is not None:
-        _need(global_scale, torch.float32, "global_scale", x.device)
-    q, s, g = out
+        _need(global_scale, torch.float32, "global_scale", x.device, (1,))
+    if out is None:
+        raise ValueError("quantize_nvfp4_noalloc takes its outputs from the caller")
+    q, s, g = _outputs(out, _nvfp4_out_specs(R, C), x.device)
     lib = load()
     _check(lib.mxq_quantize_nvfp4_noalloc(_ptr(x), R, C, _ptr(global_scale), _ptr(q), _ptr(s),
                                           _LAYOUT[scale_layout], _ptr(g), _stream(stream)))
@@ -203,19 +248,18 @@ def nvfp4_calibrate(x, running=None, workspace=None, stream=None):
     CUDA tensor (zero-initialised here when None); returned for chaining and for
     quantize_nvfp4(x, global_scale=running)."""
     torch = _torch()
-    _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
-    R, C = x.shape
-    if running is None:
-        running = torch.zeros((1,), dtype=torch.float32, device=x.device)
-    _need(running, torch.float32, "running", x.device)
-    ws_bytes = nvfp4_workspace_size(R, C)
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=x.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    R, C = _x2d(x)
+    if running is not None:
+        _need(running, torch.float32, "running", x.device, (1,))
+    ws_bytes = _workspace(workspace, x.device)
     lib = load()
-    _check(lib.mxq_nvfp4_calibrate(_ptr(x), R, C, _ptr(running), _ptr(workspace), ws_bytes, _stream(stream)))
+    with _on(stream):
+        if running is None:
+            running = torch.zeros((1,), dtype=torch.float32, device=x.device)
+        if workspace is None:
+            ws_bytes = max(nvfp4_workspace_size(R, C), 4)
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=x.device)
+        _check(lib.mxq_nvfp4_calibrate(_ptr(x), R, C, _ptr(running), _ptr(workspace), ws_bytes, _stream(stream)))
     return running
 
 
@@ -223,26 +267,18 @@ def quantize_fp8_weight(w, scale=None, out=None, workspace=None, stream=None):
     """Weight-only FP8: bf16 [R, C] -> (E4M3 codes uint8 [R, C], fp32 [1] decode
     scale).  scale: None (RN_fp32(amax / 448)) or a 1-element fp32 CUDA tensor."""
     torch = _torch()
-    _need(w, torch.bfloat16, "w")
-    if w.dim() != 2:
-        raise ValueError("w must be 2-D")
-    R, C = w.shape
+    R, C = _x2d(w, "w")
     if scale is not None:
-        _need(scale, torch.float32, "scale", w.device)
-    if out is not None:
-        q, s = out
-    else:
-        q = torch.empty((R, C), dtype=torch.uint8, device=w.device)
-        s = torch.empty((1,), dtype=torch.float32, device=w.device)
-    ws_bytes = 0
-    if scale is None:
-        ws_bytes = nvfp4_workspace_size(R, C)
-        if workspace is None:
-            workspace = torch.empty((max(ws_bytes, 4),), dtype=torch.uint8, device=w.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+        _need(scale, torch.float32, "scale", w.device, (1,))
+    ws_bytes = _workspace(workspace, w.device)
     lib = load()
-    _check(lib.mxq_quantize_fp8_weight(_ptr(w), R, C, _ptr(scale), _ptr(q), _ptr(s), _ptr(workspace), ws_bytes,
-                                       _stream(stream)))
+    with _on(stream):
+        q, s = _outputs(out, [("q", torch.uint8, (R, C)), ("scale_out", torch.float32, (1,))], w.device)
+        if scale is None and workspace is None:
+            ws_bytes = max(nvfp4_workspace_size(R, C), 4)
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=w.device)
+        _check(lib.mxq_quantize_fp8_weight(_ptr(w), R, C, _ptr(scale), _ptr(q), _ptr(s), _ptr(workspace), ws_bytes,
+                                           _stream(stream)))
     return q, s
 
 
@@ -260,21 +296,24 @@ def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e
     """C[M, N] = epi(A . W^T) in bf16 from MXFP8 operands (A [M, K], W [N, K]);
     scale_layout names the order of both scale tensors."""
     torch = _torch()
-    for t, n in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
-        _need(t, torch.uint8, n)
+    for t, n in ((a_q, "a_q"), (w_q, "w_q")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("%s must be a 2-D tensor" % n)
     M, K = a_q.shape
     N = w_q.shape[0]
-    if w_q.shape[1] != K or a_s.shape != (M, K // 32) or w_s.shape != (N, K // 32):
-        raise ValueError("operand shapes disagree")
+    _need(a_q, torch.uint8, "a_q")
+    _need(w_q, torch.uint8, "w_q", a_q.device, (N, K))
+    _need(a_s, torch.uint8, "a_s", a_q.device, (M, K // 32))
+    _need(w_s, torch.uint8, "w_s", a_q.device, (N, K // 32))
     if epi is None:
         epi = "none" if bias is None else "bias"
     e = _epi(epi, bias)
-    if bias is not None:
-        _need(bias, torch.bfloat16, "bias")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    _bias(bias, N, a_q.device)
     lib = load()
-    _check(lib.mxq_gemm_mxfp8(_ptr(a_q), _ptr(a_s), _KIND[a_kind], _ptr(w_q), _ptr(w_s), _KIND[w_kind],
-                              _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
+    with _on(stream):
+        (c,) = _outputs(out, [("out", torch.bfloat16, (M, N))], a_q.device)
+        _check(lib.mxq_gemm_mxfp8(_ptr(a_q), _ptr(a_s), _KIND[a_kind], _ptr(w_q), _ptr(w_s), _KIND[w_kind],
+                                  _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
     return c
 
 
@@ -290,34 +329,35 @@ def gemm_nvfp4(a_q, a_s, a_g, w_q, w_s, w_g, bias=None, epi=None, out=None, work
     last round be split along K.  scale_layout names the order of both scale
     tensors."""
     torch = _torch()
-    for t, n in ((a_q, "a_q"), (a_s, "a_s"), (w_q, "w_q"), (w_s, "w_s")):
-        _need(t, torch.uint8, n)
-    _need(a_g, torch.float32, "a_g")
-    _need(w_g, torch.float32, "w_g")
+    for t, n in ((a_q, "a_q"), (w_q, "w_q")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError("%s must be a 2-D tensor" % n)
     M, KP = a_q.shape
     K = 2 * KP
     N = w_q.shape[0]
-    if w_q.shape[1] != KP or a_s.shape != (M, K // 16) or w_s.shape != (N, K // 16):
-        raise ValueError("operand shapes disagree")
+    _need(a_q, torch.uint8, "a_q")
+    _need(w_q, torch.uint8, "w_q", a_q.device, (N, KP))
+    _need(a_s, torch.uint8, "a_s", a_q.device, (M, K // 16))
+    _need(w_s, torch.uint8, "w_s", a_q.device, (N, K // 16))
+    _need(a_g, torch.float32, "a_g", a_q.device, (1,))
+    _need(w_g, torch.float32, "w_g", a_q.device, (1,))
     if epi is None:
         epi = "none" if bias is None else "bias"
     e = _epi(epi, bias)
-    if bias is not None:
-        _need(bias, torch.bfloat16, "bias")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a_q.device)
+    _bias(bias, N, a_q.device)
+    nbytes = _workspace(workspace, a_q.device) if split else 0
+    ws = workspace if split else None
     lib = load()
-    ws, nbytes = None, 0
-    if split:
-        need = int(lib.mxq_gemm_nvfp4_workspace_size(M, N, K))
-        if workspace is not None:
-            _need(workspace, torch.uint8, "workspace")
-            ws, nbytes = workspace, workspace.numel()
-        elif need:
-            ws = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
-            nbytes = need
-    _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
-                              _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes,
-                              _stream(stream)))
+    with _on(stream):
+        (c,) = _outputs(out, [("out", torch.bfloat16, (M, N))], a_q.device)
+        if split and workspace is None:
+            need = int(lib.mxq_gemm_nvfp4_workspace_size(M, N, K))
+            if need:
+                ws = torch.empty((need,), dtype=torch.uint8, device=a_q.device)
+                nbytes = need
+        _check(lib.mxq_gemm_nvfp4(_ptr(a_q), _ptr(a_s), _ptr(a_g), _ptr(w_q), _ptr(w_s), _ptr(w_g),
+                                  _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _ptr(ws), nbytes,
+                                  _stream(stream)))
     return c
 
 
@@ -328,17 +368,18 @@ def quantize_fp8_v(v, heads: int, scale=None, out=None, workspace=None, stream=N
     _need(v, torch.bfloat16, "v")
     d = v.shape[-1]
     L = v.numel() // (heads * d)
-    q, s_out = out if out is not None else (torch.empty((heads, d, L), dtype=torch.uint8, device=v.device),
-                                            torch.empty((1,), dtype=torch.float32, device=v.device))
+    if scale is not None:
+        _need(scale, torch.float32, "scale", v.device, (1,))
+    nbytes = _workspace(workspace, v.device)
     lib = load()
-    ws, nbytes = None, 0
-    if scale is None:
-        nbytes = int(lib.mxq_quantize_nvfp4_workspace_size(heads * L, d))
-        ws = workspace if workspace is not None else torch.empty((max(nbytes, 4),), dtype=torch.uint8,
-                                                                 device=v.device)
-        nbytes = ws.numel()
-    _check(lib.mxq_quantize_fp8_v(_ptr(v), heads, L, d, _ptr(scale), _ptr(q), _ptr(s_out), _ptr(ws), nbytes,
-                                  _stream(stream)))
+    with _on(stream):
+        q, s_out = _outputs(out, [("vt", torch.uint8, (heads, d, L)), ("scale_out", torch.float32, (1,))], v.device)
+        ws = workspace
+        if scale is None and workspace is None:
+            nbytes = max(int(lib.mxq_quantize_nvfp4_workspace_size(heads * L, d)), 4)
+            ws = torch.empty((nbytes,), dtype=torch.uint8, device=v.device)
+        _check(lib.mxq_quantize_fp8_v(_ptr(v), heads, L, d, _ptr(scale), _ptr(q), _ptr(s_out), _ptr(ws), nbytes,
+                                      _stream(stream)))
     return q, s_out
 
 
@@ -349,34 +390,35 @@ def attention_fp8(q, q_scale, k, k_scale, vt, v_scale, heads: int, out=None, str
     for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
         _need(t, torch.uint8, n)
     for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
-        _need(t, torch.float32, n)
+        _need(t, torch.float32, n, q.device, (1,))
     d = q.shape[-1]
     L = q.numel() // (heads * d)
     if k.numel() != q.numel() or vt.numel() != q.numel():
         raise ValueError("q, k, vt sizes disagree")
-    o = out if out is not None else torch.empty((heads * L, d), dtype=torch.bfloat16, device=q.device)
-    _check(load().mxq_attention_fp8(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(vt), _ptr(v_scale),
-                                    heads, L, d, _ptr(o), _stream(stream)))
+    lib = load()
+    with _on(stream):
+        (o,) = _outputs(out, [("out", torch.bfloat16, (heads * L, d))], q.device)
+        _check(lib.mxq_attention_fp8(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(vt), _ptr(v_scale),
+                                     heads, L, d, _ptr(o), _stream(stream)))
     return o
 
 
 def gemm_bf16_fp8w(a, w_q, w_scale, bias=None, epi=None, out=None, stream=None):
     """Weight-only FP8: C[M, N] = epi(s_w A . val(W)^T) in bf16, A bf16 [M, K], W E4M3 [N, K]."""
     torch = _torch()
-    _need(a, torch.bfloat16, "a")
-    _need(w_q, torch.uint8, "w_q")
-    _need(w_scale, torch.float32, "w_scale")
-    M, K = a.shape
+    M, K = _x2d(a, "a")
+    if not isinstance(w_q, torch.Tensor) or w_q.dim() != 2:
+        raise ValueError("w_q must be a 2-D tensor")
     N = w_q.shape[0]
-    if w_q.shape[1] != K:
-        raise ValueError("operand shapes disagree")
+    _need(w_q, torch.uint8, "w_q", a.device, (N, K))
+    _need(w_scale, torch.float32, "w_scale", a.device, (1,))
     if epi is None:
         epi = "none" if bias is None else "bias"
     e = _epi(epi, bias)
-    if bias is not None:
-        _need(bias, torch.bfloat16, "bias")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _bias(bias, N, a.device)
     lib = load()
-    _check(lib.mxq_gemm_bf16_fp8w(_ptr(a), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(bias), e, _ptr(c),
-                                  _stream(stream)))
+    with _on(stream):
+        (c,) = _outputs(out, [("out", torch.bfloat16, (M, N))], a.device)
+        _check(lib.mxq_gemm_bf16_fp8w(_ptr(a), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(bias), e, _ptr(c),
+                                      _stream(stream)))
     return c

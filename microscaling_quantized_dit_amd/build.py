@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxq.so")
 PROBES_LIB = os.path.join(PKG, "libmxq_probes.so")
-PROBES_SOURCES = ["probes.hip"]
+# the probes library also holds a probe build of the MXFP8 GEMM (MXQ_PROBE_BUILD)
+PROBES_SOURCES = ["probes.hip", "gemm_mxfp8.hip"]
 SOURCES = ["quant_mxfp8.hip", "quant_nvfp4.hip", "gemm_mxfp8.hip", "gemm_nvfp4.hip", "gemm_w8.hip", "gemm_fixup.hip",
            "attention_fp8.hip", "mxq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,17 +32,19 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    def compile_one(job):
+        src, probe = job
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + (".probe.o" if probe else ".o"))
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        defs = ["-DMXQ_PROBE_BUILD"] if probe else []
+        cmd = [HIPCC] + FLAGS + defs + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         return obj
 
     with ThreadPoolExecutor(len(SOURCES) + len(PROBES_SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES + PROBES_SOURCES))
+        objs = list(ex.map(compile_one, [(f, False) for f in SOURCES] + [(f, True) for f in PROBES_SOURCES]))
     for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PROBES_LIB, objs[len(SOURCES):])):
         tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + lib_objs

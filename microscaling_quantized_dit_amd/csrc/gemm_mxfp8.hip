@@ -62,7 +62,11 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int R, int x, int S, in
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int AK, int WK, int EPI, bool TILED>
+// A_READS: how many times each stage's A codes are DMA'd into LDS (the same bytes
+// to the same place).  The library uses 1; the measurement probes build a 2
+// (bf16-sized A traffic with no quantization work), the lower bound of fusing the
+// activation quantizer into this GEMM's prologue.
+template <int AK, int WK, int EPI, bool TILED, int A_READS = 1>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as_, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ ws, const uint16_t* __restrict__ bias, uint16_t* __restrict__ c, int M, int N,
@@ -133,8 +137,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     for (int j = 0; j < 8; ++j) {
       const int vo = (j & 1) ? voff1 : voff0;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(base + j * 8 * kBK), 16, vo, off_w + j * 8 * K, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 8 * kBK), 16, vo,
-                                               off_a + j * 8 * K, 0, 0);
+#pragma unroll
+      for (int rep = 0; rep < A_READS; ++rep)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + kOperand + j * 8 * kBK), 16, vo,
+                                                 off_a + j * 8 * K, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sc + wave * 64), 4, vsc, off_sw, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc, off_sa, 0, 0);
@@ -328,6 +334,22 @@ hipError_t launch_kinds(const void* a_q, const void* a_s, const void* w_q, const
 }
 
 }  // namespace
+
+#ifdef MXQ_PROBE_BUILD
+// Measurement probe (built into libmxq_probes.so only): E4M3 x E4M3, no epilogue,
+// tiled scales, each A stage DMA'd twice.
+hipError_t launch_gemm_mxfp8_a_twice(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t M,
+                                     int64_t N, int64_t K, void* c, hipStream_t stream) {
+  const int m = (int)M, n = (int)N, k = (int)K;
+  const int tiles = ((m + kTile - 1) / kTile) * ((n + kTile - 1) / kTile);
+  const int cus = device_compute_units();
+  const int grid_n = ((k / kBK) % 2 != 0 || tiles < cus) ? tiles : cus;
+  hipLaunchKernelGGL((k_gemm_mxfp8<0, 0, 0, true, 2>), dim3(grid_n), dim3(kThreads), 0, stream, (const uint8_t*)a_q,
+                     (const uint8_t*)a_s, (const uint8_t*)w_q, (const uint8_t*)w_s, (const uint16_t*)nullptr,
+                     (uint16_t*)c, m, n, k);
+  return hipGetLastError();
+}
+#endif
 
 // Shapes reaching here are validated: M, N, K positive multiples of 128, kinds 0/1, epi 0..2.
 // Partial 256-tiles (M or N = 128 mod 256) skip the stores of their missing half.

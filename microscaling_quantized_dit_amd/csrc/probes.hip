@@ -13,6 +13,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
+namespace mxq {
+hipError_t launch_gemm_mxfp8_a_twice(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t M,
+                                     int64_t N, int64_t K, void* c, hipStream_t stream);
+// Compute units of the current device (the GEMM launcher's persistent grid).
+int device_compute_units() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+      n = 256;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+}  // namespace mxq
+
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -109,11 +129,23 @@ __global__ __launch_bounds__(256) void k_loop_f16(int iters, float* sink, uint64
   sink[id] = s;
 }
 
-// Streaming copy of n16 16-byte chunks, grid-stride, nontemporal both ways.
+// Streaming copy of n16 16-byte chunks: each workgroup moves consecutive slabs of
+// 4 x 256 chunks (four 16-byte loads in flight per thread, then four stores),
+// nontemporal both ways; the remainder chunk by chunk.
 __global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+  const int64_t slab = 4 * 256;
+  const int64_t n_slabs = n16 / slab;
+  for (int64_t b = blockIdx.x; b < n_slabs; b += gridDim.x) {
+    const int64_t base = b * slab + threadIdx.x;
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load((const u32x4*)(src + base + 256 * u));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) __builtin_nontemporal_store(v[u], (u32x4*)(dst + base + 256 * u));
+  }
+  for (int64_t i = n_slabs * slab + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
     __builtin_nontemporal_store(__builtin_nontemporal_load((const u32x4*)(src + i)), (u32x4*)(dst + i));
 }
 
@@ -190,6 +222,14 @@ int probe_mfma_once_16(const void* a, const void* b, const float* c_in, float* o
   hipLaunchKernelGGL(k_once_16, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint16_t*)a, (const uint16_t*)b,
                      c_in, out, kind);
   return (int)hipGetLastError();
+}
+
+// The MXFP8 GEMM (E4M3, tiled scales, no epilogue) with each A stage DMA'd twice:
+// the lower bound of a GEMM that reads bf16 activations to quantize them itself.
+// Operands validated by the caller: M, N, K multiples of 128, operands < 2 GiB.
+int probe_gemm_mxfp8_a_twice(const void* a_q, const void* a_s, const void* w_q, const void* w_s, int64_t M,
+                             int64_t N, int64_t K, void* c, void* stream) {
+  return (int)mxq::launch_gemm_mxfp8_a_twice(a_q, a_s, w_q, w_s, M, N, K, c, (hipStream_t)stream);
 }
 
 // Rate of the constant clock s_memrealtime counts (Hz).

@@ -26,8 +26,10 @@ def load():
         lib.probe_copy.argtypes = [P, P, i64, i32, P]
         lib.probe_mfma_once_fp8.argtypes = [P, P, P, P, P]
         lib.probe_mfma_once_16.argtypes = [P, P, P, P, i32, P]
+        lib.probe_gemm_mxfp8_a_twice.argtypes = [P, P, P, P, i64, i64, i64, P, P]
         lib.probe_wall_clock_hz.restype = i64
-        for f in ("probe_mfma_loop", "probe_copy", "probe_mfma_once_fp8", "probe_mfma_once_16"):
+        for f in ("probe_mfma_loop", "probe_copy", "probe_mfma_once_fp8", "probe_mfma_once_16",
+                  "probe_gemm_mxfp8_a_twice"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -87,13 +89,14 @@ def hbm_copy(n_bytes: int = 1 << 30, reps: int = 5):
     src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    _check(lib.probe_copy(_ptr(src), _ptr(dst), n_bytes, cus * 8, _stream()))
+    blocks = cus * 4
+    _check(lib.probe_copy(_ptr(src), _ptr(dst), n_bytes, blocks, _stream()))
     stream = torch.cuda.current_stream()
     best = 0.0
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        _check(lib.probe_copy(_ptr(src), _ptr(dst), n_bytes, cus * 8, _stream()))
+        _check(lib.probe_copy(_ptr(src), _ptr(dst), n_bytes, blocks, _stream()))
         b.record(stream)
         torch.cuda.synchronize()
         best = max(best, 2 * n_bytes / (a.elapsed_time(b) * 1e-3) / 1e9)
@@ -127,3 +130,21 @@ def mfma_once_16(a_bits, b_bits, kind: str, c=None):
     out = torch.empty((32, 32), dtype=torch.float32, device="cuda")
     _check(lib.probe_mfma_once_16(_ptr(da), _ptr(db), _ptr(dc), _ptr(out), 0 if kind == "fp16" else 1, _stream()))
     return out.cpu().numpy().astype(np.float64)
+
+
+def gemm_mxfp8_a_twice(a_q, a_s, w_q, w_s, out):
+    """The MXFP8 GEMM (E4M3, tiled scales, no epilogue) with every A stage DMA'd
+    twice -- a GEMM that reads its activation at bf16 size, without the work of
+    quantizing it: the lower bound of fusing the quantizer into the prologue.
+    Operands as for gemm_mxfp8 with scale_layout="tiled"; out bf16 [M, N]."""
+    import torch
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    for t in (a_q, a_s, w_q, w_s, out):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("operands must be contiguous GPU tensors")
+    if M % 128 or N % 128 or K % 128 or tuple(out.shape) != (M, N) or out.dtype != torch.bfloat16:
+        raise ValueError("M, N, K multiples of 128 and out bf16 [M, N] required")
+    _check(load().probe_gemm_mxfp8_a_twice(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(out),
+                                           _stream()))
+    return out
