@@ -95,10 +95,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
   for (int u = 0; u < U; ++u) {
     const int64_t c = chunk(u);
     // Lanes 4j..4j+3 hold chunks 4j'..4j'+3 of one 32-block (n_chunks % 4 == 0,
-    // so a group is entirely in or entirely out of range).
+    // so a group is entirely in or entirely out of range); their maxima meet
+    // through two DPP swaps within the quad, [1,0,3,2] then [2,3,0,1].
     uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
     const int E = block_exponent<KIND>(m);
     const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, normal
     uint2 out;

@@ -223,46 +223,84 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   const float r6_hi = (float)(r6 * (1.0 + 0x1p-19));
   const bool fast6 = r6 < 0x1p126 && r6 > 0x1p-126;
 
+  // The chunks go through each phase in groups of kGroup, so that the fast path is
+  // straight-line code and the exact fallbacks are entered once per phase and
+  // group, only when some lane needs them (groups of two keep the kernel within
+  // the registers of eight waves per SIMD).
+  constexpr int kGroup = 2;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t c = chunk(u);
-    // lanes 2j, 2j+1 hold the two halves of one 16-block (n_chunks is even)
-    uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    const float amax_b = __uint_as_float(m << 16);
+  for (int g0 = 0; g0 < kUnroll; g0 += kGroup) {
+    // ---- block maxima: lanes 2j, 2j+1 hold the two halves of one 16-block
+    // (n_chunks is even); their maxima meet through a DPP swap within lane pairs
+    float amax_b[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[g0 + i]));
+      const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+      amax_b[i] = __uint_as_float(max(m, other) << 16);
+    }
 
     // ---- S_b = RN_E4M3(amax_b / (6 s_g)), from the two bracketing quotients
-    int sb;
-    {
-      float ql = __builtin_amdgcn_fmed3f(amax_b * r6_lo, 0.0f, 448.0f);
-      float qh = __builtin_amdgcn_fmed3f(amax_b * r6_hi, 0.0f, 448.0f);
-      int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ql, qh, 0, false);
-      int cl = pk & 0xFF, ch = (pk >> 8) & 0xFF;
-      sb = cl;
-      if (__builtin_expect(!fast6, 0)) {
-        sb = exact_block_scale((double)amax_b, six_sg);
-      } else if (__builtin_expect(cl != ch, 0)) {
-        // one midpoint between the adjacent codes cl < ch: compare exactly
-        const float mk = (__builtin_amdgcn_cvt_f32_fp8(cl, 0) + __builtin_amdgcn_cvt_f32_fp8(ch, 0)) * 3.0f;
-        sb = round_up_at(amax_b, mk, sg, (ch & 1) == 0) ? ch : cl;
+    int sb[kGroup], sb_hi[kGroup];
+    bool exact_sb = !fast6;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const float ql = __builtin_amdgcn_fmed3f(amax_b[i] * r6_lo, 0.0f, 448.0f);
+      const float qh = __builtin_amdgcn_fmed3f(amax_b[i] * r6_hi, 0.0f, 448.0f);
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ql, qh, 0, false);
+      sb[i] = pk & 0xFF;
+      sb_hi[i] = (pk >> 8) & 0xFF;
+      exact_sb |= sb[i] != sb_hi[i];
+    }
+    if (__builtin_expect(exact_sb, 0)) {
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        const int cl = sb[i], ch = sb_hi[i];
+        if (!fast6) {
+          sb[i] = exact_block_scale((double)amax_b[i], six_sg);
+        } else if (cl != ch) {
+          // one midpoint between the adjacent codes cl < ch: compare exactly
+          const float mk = (__builtin_amdgcn_cvt_f32_fp8(cl, 0) + __builtin_amdgcn_cvt_f32_fp8(ch, 0)) * 3.0f;
+          sb[i] = round_up_at(amax_b[i], mk, sg, (ch & 1) == 0) ? ch : cl;
+        }
       }
     }
-    const float S = __builtin_amdgcn_cvt_f32_fp8(sb, 0);      // E4M3 -> fp32, exact
 
     // ---- codes: x / (S s_g), bracketed.  S = 0 gives r = 0 and signed zeros.
-    const float D = S * sg;
-    const float r = S == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(D);   // <= 1 ulp
-    uint32_t codes = encode8(v[u], r * (1.0f - 0x1p-19f));
-    const uint32_t hi = encode8(v[u], r * (1.0f + 0x1p-19f));
-    // fp64 path for a tiny divisor (reciprocal or two-product out of range) or a
-    // saturated block scale (only a static s_g can then push quotients far past
-    // 6); otherwise a midpoint between the brackets is settled exactly in fp32
-    const bool slow = S != 0.0f && (!(D >= 0x1p-100f) || sb == 126);
-    if (__builtin_expect(slow, 0)) codes = exact_chunk(v[u], S, sg);
-    else if (__builtin_expect(S != 0.0f && codes != hi, 0)) codes = resolve_chunk(v[u], codes, hi, S, sg);
-    if (TILED || c < n_chunks) {
-      dev::store_nt(codes, q + c);
-      if ((t & 1) == 0) s[TILED ? ts.scale(u) : c >> 1] = (uint8_t)sb;
+    uint32_t codes[kGroup], codes_hi[kGroup];
+    float S[kGroup];
+    bool exact_c = false;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      S[i] = __builtin_amdgcn_cvt_f32_fp8(sb[i], 0);        // E4M3 -> fp32, exact
+      const float D = S[i] * sg;
+      const float r = S[i] == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(D);   // <= 1 ulp
+      codes[i] = encode8(v[g0 + i], r * (1.0f - 0x1p-19f));
+      codes_hi[i] = encode8(v[g0 + i], r * (1.0f + 0x1p-19f));
+      // the fp64 path serves a tiny divisor (reciprocal or two-product out of
+      // range) or a saturated block scale (only a static s_g can then push
+      // quotients far past 6); otherwise a midpoint between the brackets is
+      // settled exactly in fp32
+      exact_c |= S[i] != 0.0f && (codes[i] != codes_hi[i] || !(D >= 0x1p-100f) || sb[i] == 126);
+    }
+    if (__builtin_expect(exact_c, 0)) {
+#pragma unroll
+      for (int i = 0; i < kGroup; ++i) {
+        if (S[i] == 0.0f) continue;
+        const float D = S[i] * sg;
+        if (!(D >= 0x1p-100f) || sb[i] == 126) codes[i] = exact_chunk(v[g0 + i], S[i], sg);
+        else if (codes[i] != codes_hi[i]) codes[i] = resolve_chunk(v[g0 + i], codes[i], codes_hi[i], S[i], sg);
+      }
+    }
+
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const int u = g0 + i;
+      const int64_t c = chunk(u);
+      if (TILED || c < n_chunks) {
+        dev::store_nt(codes[i], q + c);
+        if ((t & 1) == 0) s[TILED ? ts.scale(u) : c >> 1] = (uint8_t)sb[i];
+      }
     }
   }
 }
