@@ -25,7 +25,8 @@
 // (TILED, mxq_internal.h) a wave's 64 dwords are one contiguous 256-byte run.
 // Each stage is split at a mid-stage barrier so that one
 // half's MFMAs overlap the other half's fragment reads and the DMA two stages
-// ahead.  The kernel is persistent (one workgroup per CU): a workgroup walks its
+// ahead; one dword of every row segment three stages ahead is loaded too, which
+// brings those cache lines into L2 before their DMA is issued.  The kernel is persistent (one workgroup per CU): a workgroup walks its
 // tiles as one stream of stages, so the next tile's first stages are in flight
 // during the previous tile's epilogue.  Tiles are ordered so that each XCD (one
 // L2) works on a contiguous range, in groups of four M-tiles.
@@ -47,6 +48,10 @@ constexpr int kOperand = kTile * kBK;          // 32 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
 constexpr int kGroupM = 4;
 constexpr int kCStage = dev::epilogue_lds_bytes(64);   // epilogue staging per wave
+// Mid-stage wait: every vector memory operation but the newest two (the stage's
+// L2 prefetch, issued right after its DMA) and every LDS read.  Vector memory
+// loads retire in issue order, and no store is in flight inside the K loop.
+constexpr int kWaitDmaLeavePrefetch = dev::waitcnt_imm(2, 0);
 
 // XOR swizzle of the eight 16-byte chunks of an LDS row: row R keeps logical
 // chunk c at physical chunk c ^ swz(R).  The 16 rows read by one quarter-wave
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // dwords (4 MX blocks of every row) follow with one 4-byte-per-lane load per
   // operand: lane i of wave w -> row 64w + i (TILED: dword i of the run of the
   // wave's 64-row block and this stage).
-  int voff0, voff1, vsc;
+  int voff0, voff1, vsc, vpf;
   // Every load stays inside its operand.  A wave's 64 rows lie wholly inside or
   // wholly past M (N), both being multiples of 128; rows past the end, and the
   // stages after the workgroup's last tile (valid == false), read rows [0, 64)
@@ -146,6 +151,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(sc + kTile + wave * 64), 4, vsc, off_sa, 0, 0);
   };
 
+  // L2 prefetch of a later stage: one dword of every 128-byte row segment (one
+  // cache line) of the wave's 64 rows of W and of A, as two 4-byte LDS-DMA loads.
+  // They hold no registers, so the waits below can leave them in flight.  Their
+  // bytes land in the first 256 bytes of the wave's own epilogue staging area,
+  // which nothing reads inside the K loop; every prefetch has retired (vmcnt 0)
+  // before the epilogue writes there, and the epilogue's LDS accesses have retired
+  // (lgkmcnt 0, barrier) before the next tile issues its first prefetch.
+  auto prefetch = [&](int m0, int n0, int k0, bool valid) {
+    const int rw0 = n0 + wave * 64, ra0 = m0 + wave * 64;
+    const bool vw = valid && rw0 < N, va = valid && ra0 < M;
+    const int off_w = vw ? rw0 * K + k0 : 0, off_a = va ? ra0 * K + k0 : 0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(c_lds + wave * kCStage), 4, vpf, off_w, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(c_lds + wave * kCStage), 4, vpf, off_a, 0, 0);
+  };
+
   int x, wrow, arow;
   // The lane-derived offsets are recomputed at the top of every tile from the lane
   // id (mbcnt, in a volatile asm block so that it is not hoisted): otherwise they
@@ -160,6 +180,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     voff0 = lrow * K + cx * 16;
     voff1 = lrow * K + (cx ^ 4) * 16;
     vsc = TILED ? lane * 4 : lane * KB;
+    vpf = lane * K;
     x = swz(r);
     wrow = wn * 128 + r;
     arow = wm * 128 + r;
@@ -186,13 +207,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   // One stage (buffer cur holds it; nxt holds the next one, possibly of the next tile):
   //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of this stage
   //   B: wait for the next stage's DMA and this wave's reads, barrier (cur is now
-  //      free in every wave, the next stage visible in nxt); a tile's first stage
-  //      finds the next stage's DMA retired before the previous tile's epilogue and
-  //      waits for its reads only, leaving the epilogue's stores in flight
+  //      free in every wave, the next stage visible in nxt).  The wait depends on
+  //      the stage's kind: a tile's first stage (kind 0) finds the next stage's DMA
+  //      retired before the previous tile's epilogue and waits for its reads only,
+  //      leaving the epilogue's stores in flight; its second stage (kind 1) waits
+  //      for every operation, since loads and those stores may retire out of order;
+  //      the others (kind 2) leave the newest prefetch in flight.
   //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of the next stage;
-  //      DMA of the stage after next (given by dm0, dn0, dk0, dvalid) into cur.
-  auto stage = [&](auto first_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
-                   int dm0, int dn0, int dk0, bool dvalid) {
+  //      DMA of the stage after next (given by dm0, dn0, dk0, dvalid) into cur,
+  //      then the L2 prefetch of the stage after that (pm0, pn0, pk0, pvalid).
+  auto stage = [&](auto kind_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
+                   int dm0, int dn0, int dk0, bool dvalid, int pm0, int pn0, int pk0, bool pvalid) {
     // ---- A
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -212,8 +237,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- B
-    if constexpr (decltype(first_)::value) __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);
-    else __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    constexpr int kind = decltype(kind_)::value;
+    if constexpr (kind == 0) __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);
+    else if constexpr (kind == 1) __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
+    else __builtin_amdgcn_s_waitcnt(kWaitDmaLeavePrefetch);
     dev::lds_barrier();
     // ---- C
     read_scales(snxt);
@@ -223,6 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       f0a[i] = frag(nxt + kOperand, arow + 32 * i, x, 0, g);
     }
     dma_stage(cur, scur, dm0, dn0, dk0, dvalid);
+    prefetch(pm0, pn0, pk0, pvalid);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -266,11 +294,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
 
   // Global stage g uses buffer g & 1.  With an even number of stages per tile every
   // tile starts in buffer 0; with an odd number the launcher gives each workgroup a
-  // single tile.  The K loop is unrolled by two so that every LDS pointer is a fixed
-  // object, and the DMA target of stage kt + 2 is chosen with scalar selects (no
-  // branch inside the loop body).
-  using First = std::integral_constant<bool, true>;
-  using Later = std::integral_constant<bool, false>;
+  // single tile.  A tile's first two stages are peeled; the rest of the K loop is
+  // unrolled by two so that every LDS pointer is a fixed object, and the DMA and
+  // prefetch targets are chosen with scalar selects (no branch inside the loop body).
+  using First = std::integral_constant<int, 0>;
+  using Second = std::integral_constant<int, 1>;
+  using Later = std::integral_constant<int, 2>;
   for (int ti = 0; ti < my_tiles; ++ti) {
     lane_setup(true);
     const bool has_next = ti + 1 < my_tiles;
@@ -281,23 +310,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    auto one = [&](auto first_, uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
-      const int kk = kt + 2;
-      const bool nx = kk >= nk;
-      stage(first_, acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK,
-            !nx || has_next);
+    auto one = [&](auto kind_, uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
+      const int kk = kt + 2, kp = kt + 3;
+      const bool nx = kk >= nk, nxp = kp >= nk;
+      stage(kind_, acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next,
+            nxp ? m0n : m0, nxp ? n0n : n0, (nxp ? kp - nk : kp) * kBK, !nxp || has_next);
     };
     one(First(), lds0, lds1, sc0, sc1, 0);
     // the tile's bias, read by this wave's epilogue from LDS, so that no global load
     // there queues behind the epilogue's own stores (issued after the first stage:
     // its reads then need not wait for it)
     if constexpr (EPI >= 1) dev::load_bias(rb, bias_lds + wave * 1024, n0 + wn * 128, lane);
-    int kt = 1;
+    if (nk > 1) one(Second(), lds1, lds0, sc1, sc0, 1);
+    int kt = 2;
     for (; kt + 1 < nk; kt += 2) {
-      one(Later(), lds1, lds0, sc1, sc0, kt);
-      one(Later(), lds0, lds1, sc0, sc1, kt + 1);
+      one(Later(), lds0, lds1, sc0, sc1, kt);
+      one(Later(), lds1, lds0, sc1, sc0, kt + 1);
     }
-    if (kt < nk) one(Later(), lds1, lds0, sc1, sc0, kt);
+    if (kt < nk) one(Later(), lds0, lds1, sc0, sc1, kt);
     // Retire the next tile's first two stages of DMA now: the stores below share
     // the counter, and the next tile's first stage then waits for none of them.
     __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
