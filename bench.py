@@ -106,6 +106,87 @@ def step_dispatches():
     return out
 
 
+def _step_rows(db):
+    """Per dispatch of the step in a rocprofv3 counter database: (op, kernel,
+    duration in ns, {counter: value summed over its instances}).  The step's
+    dispatches are the ones right after the 1 GiB calibration copy; a GEMM's split
+    and fixup dispatches, when there are any, are counted with it (durations
+    added)."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select k.dispatch_id, k.name, k.end - k.start, p.counter_name, sum(p.counter_value) "
+                       "from pmc_events p join kernels k on k.dispatch_id = p.dispatch_id "
+                       "group by k.dispatch_id, p.counter_name order by k.dispatch_id").fetchall()
+    disp = {}
+    for did, name, dur, counter, value in rows:
+        short = name.replace("mxq::(anonymous namespace)::", "").replace("void ", "").split("(")[0].strip()
+        e = disp.setdefault(did, [short, float(dur), {}])
+        e[2][counter] = float(value)
+    order = sorted(disp)
+    copies = [i for i, d in enumerate(order) if "copyBuffer" in disp[d][0]]
+    if not copies:
+        raise SystemExit("no calibration copy in %s" % db)
+    j = max(copies, key=lambda i: disp[order[i]][1]) + 1
+    out = []
+    for op, kernel in step_dispatches():
+        if j >= len(order) or disp[order[j]][0] != kernel:
+            raise SystemExit("%s: expected %s at dispatch %d, found %s" % (
+                db, kernel, j, disp[order[j]][0] if j < len(order) else None))
+        name, dur, vals = disp[order[j]]
+        vals = dict(vals)
+        j += 1
+        while j < len(order) and disp[order[j]][0].startswith(SPLIT_KERNELS):
+            dur += disp[order[j]][1]
+            for c, v in disp[order[j]][2].items():
+                vals[c] = vals.get(c, 0.0) + v
+            j += 1
+        out.append((op, name, dur, vals))
+    return out
+
+
+XCDS, SIMDS = 8, 1024          # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def counter_table(dbs):
+    """Markdown table of the step's dispatches from rocprofv3 counter runs of
+        python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration
+    (each database one pass; GRBM_GUI_ACTIVE in every pass).  Derived columns:
+      clock   = GRBM_GUI_ACTIVE / 8 / duration (the GPU clock over the dispatch)
+      MFMA    = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)
+      VALU    = 4 SQ_ACTIVE_INST_VALU / (1024 x GRBM_GUI_ACTIVE / 8)
+      LDS cf  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of LDS cycles stalled)
+      TA      = TA_BUSY_avr / (GRBM_GUI_ACTIVE / 8)
+      L2 hit  = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"""
+    merged = None
+    for db in dbs:
+        rows = _step_rows(db)
+        if merged is None:
+            merged = [(op, k, [d], dict(v)) for op, k, d, v in rows]
+        else:
+            for m, (op, k, d, v) in zip(merged, rows):
+                m[2].append(d)
+                for c, x in v.items():
+                    if c != "GRBM_GUI_ACTIVE":
+                        m[3][c] = x
+    print("| Op | Kernel | us | clock MHz | MFMA | VALU | LDS cf | TA | L2 hit |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|---:|")
+    for op, kernel, durs, v in merged:
+        ns = sum(durs) / len(durs)
+        g = v.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+
+        def ratio(num, den):
+            return "%.2f" % (num / den) if den else "-"
+        mfma = ratio(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), SIMDS * g) if "SQ_VALU_MFMA_BUSY_CYCLES" in v else "-"
+        valu = ratio(4 * v.get("SQ_ACTIVE_INST_VALU", 0.0), SIMDS * g) if "SQ_ACTIVE_INST_VALU" in v else "-"
+        lds = ratio(v.get("SQ_LDS_BANK_CONFLICT", 0.0), v.get("SQ_LDS_IDX_ACTIVE", 0.0)) \
+            if "SQ_LDS_BANK_CONFLICT" in v else "-"
+        ta = ratio(v.get("TA_BUSY_avr", 0.0), g) if "TA_BUSY_avr" in v else "-"
+        hit = ratio(v.get("TCC_HIT_sum", 0.0), v.get("TCC_HIT_sum", 0.0) + v.get("TCC_MISS_sum", 0.0)) \
+            if "TCC_HIT_sum" in v else "-"
+        print("| %s | `%s` | %.1f | %.0f | %s | %s | %s | %s | %s |" % (
+            op, kernel, ns / 1e3, g / ns * 1e3 if ns else 0.0, mfma, valu, lds, ta, hit))
+
+
 def record_traffic(fetch_db, write_db):
     """profiles/hbm_traffic.json from the two counter runs
         rocprofv3 --pmc FETCH_SIZE --kernel-trace ... -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration
@@ -189,6 +270,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=1536, help="rows per linear in the CPU-baseline sample")
     p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/hbm_traffic.json from two rocprofv3 counter databases (no GPU needed)")
+    p.add_argument("--counter-table", nargs="+", metavar="DB",
+                   help="print the step's per-dispatch counter table from rocprofv3 counter databases (no GPU needed)")
     return p.parse_args()
 
 
@@ -644,11 +727,14 @@ def cpu_baseline(rows_per_linear: int):
 
 def main():
     args = parse()
+    if args.counter_table:
+        counter_table(args.counter_table)
+        return
     if args.record_traffic:
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the hot path runs on a single MI355X); "
+        print("bench.py measures one GPU (the hot path runs on a single MI355X); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

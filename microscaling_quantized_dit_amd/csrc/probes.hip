@@ -191,6 +191,13 @@ __global__ __launch_bounds__(64) void k_once_16(const uint16_t* a, const uint16_
 
 }  // namespace
 
+// The hardware base-2 exponential (v_exp_f32, what the attention kernel's
+// probabilities go through) on n given arguments.
+__global__ __launch_bounds__(256) void k_exp2(const float* x, float* y, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = __builtin_amdgcn_exp2f(x[i]);
+}
+
 extern "C" {
 
 // MFMA loops: `blocks` workgroups of 256 threads, `iters` rounds of 8 MFMAs per
@@ -238,6 +245,13 @@ int64_t probe_wall_clock_hz(void) {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
   return (int64_t)khz * 1000;
+}
+
+// y[i] = v_exp_f32(x[i]) for i < n (device fp32 arrays).
+int probe_exp2(const float* x, float* y, int n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(k_exp2, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, x, y, n);
+  return (int)hipGetLastError();
 }
 
 }  // extern "C"

@@ -28,8 +28,9 @@ def load():
         lib.probe_mfma_once_16.argtypes = [P, P, P, P, i32, P]
         lib.probe_gemm_mxfp8_a_twice.argtypes = [P, P, P, P, i64, i64, i64, P, P]
         lib.probe_wall_clock_hz.restype = i64
+        lib.probe_exp2.argtypes = [P, P, i32, P]
         for f in ("probe_mfma_loop", "probe_copy", "probe_mfma_once_fp8", "probe_mfma_once_16",
-                  "probe_gemm_mxfp8_a_twice"):
+                  "probe_gemm_mxfp8_a_twice", "probe_exp2"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -148,3 +149,13 @@ def gemm_mxfp8_a_twice(a_q, a_s, w_q, w_s, out):
     _check(load().probe_gemm_mxfp8_a_twice(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(out),
                                            _stream()))
     return out
+
+
+def exp2(x):
+    """v_exp_f32 of every element of a contiguous fp32 CUDA tensor (a new tensor)."""
+    import torch
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    y = torch.empty_like(x)
+    _check(load().probe_exp2(_ptr(x), _ptr(y), x.numel(), _stream()))
+    return y

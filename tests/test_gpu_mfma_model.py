@@ -10,7 +10,9 @@ exact fp64 sum of exactly representable products).
     consecutive K positions, each group's largest product exact and every other
     one losing at most min(|p|, 2^-12 x the group's largest), plus 2^-22 sum |p|.
   * v_mfma_f32_32x32x16_{f16,bf16} (the NVFP4 and weight-only FP8 GEMMs'
-    instructions) stay within 2^-21 sum |p| of the exact sum."""
+    instructions) stay within 2^-21 sum |p| of the exact sum.
+  * v_exp_f32 (the attention kernel's exponential) is within 2^-21 relative of
+    2^x, the allowance the attention bound takes for it."""
 import numpy as np
 import pytest
 
@@ -102,3 +104,17 @@ def test_16bit_accumulation_close_to_fp32(probes, kind):
         p = av[:, None, :] * bv[None, :, :]
         err = np.abs(d - p.sum(axis=-1))
         assert np.all(err <= 2.0 ** -21 * np.abs(p).sum(axis=-1)), kind
+
+
+def test_exp2_accuracy(probes):
+    """v_exp_f32 against 2^x in fp64 (exact to far below fp32's precision) on every
+    argument the attention kernel can feed it: [-126, 9) (256 P <= 2^8 before the
+    scaling margin; below 2^-126 the code underflows anyway), 2^20 seeded values
+    plus every integer and half-integer of the range."""
+    import torch
+    rng = np.random.RandomState(5)
+    x = np.concatenate([rng.uniform(-126.0, 9.0, size=1 << 20), np.arange(-126.0, 9.0, 0.5)]).astype(np.float32)
+    y = probes.exp2(torch.from_numpy(x).cuda()).cpu().numpy().astype(np.float64)
+    ref = np.exp2(x.astype(np.float64))
+    rel = np.abs(y - ref) / ref
+    assert rel.max() <= 2.0 ** -21, (rel.max(), x[np.argmax(rel)])
