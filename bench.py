@@ -97,7 +97,7 @@ def step_dispatches():
     out = []
     for name, _, _, epi in MX_LINEARS:
         out.append(("quant_mxfp8_" + name, "k_quant_mxfp8<0, %s>" % TILED_NAME))
-        out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d, %s>" % ({"none": 0, "bias": 1, "bias_gelu": 2}[epi],
+        out.append(("gemm_mxfp8_" + name, "k_gemm_mxfp8<0, 0, %d, %s, 1>" % ({"none": 0, "bias": 1, "bias_gelu": 2}[epi],
                                                                            TILED_NAME)))
     for name, _, _, epi in NV_LINEARS:
         out.append(("quant_nvfp4_" + name, "k_amax_partials"))
@@ -142,6 +142,65 @@ def _step_rows(db):
             j += 1
         out.append((op, name, dur, vals))
     return out
+
+
+def trace_table(db):
+    """Markdown summary of a rocprofv3 kernel trace of
+        python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline
+    (1) per kernel function: calls, total and average duration, share of the
+    traced GPU time (kernels under 0.2% left out); (2) per op of the step: the mean
+    duration over every complete step sequence found in the trace (an op's split
+    and fixup dispatches added to it), and the mean per launch of each step kernel
+    over those sequences."""
+    import sqlite3
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select name, end - start from kernels order by start").fetchall()
+
+    def short(name):
+        return name.replace("mxq::(anonymous namespace)::", "").replace("void ", "").split("(")[0].strip()
+    names = [short(n) for n, _ in rows]
+    durs = [float(d) for _, d in rows]
+    total = sum(durs)
+    stats = {}
+    for n, d in zip(names, durs):
+        e = stats.setdefault(n, [0, 0.0, float("inf"), 0.0])
+        e[0] += 1
+        e[1] += d
+        e[2] = min(e[2], d)
+        e[3] = max(e[3], d)
+    print("| Kernel | Calls | Total (ns) | Average (ns) | % | Min (ns) | Max (ns) |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for n, (c, t, lo, hi) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        if t / total < 0.002:
+            continue
+        print("| `%s` | %d | %.0f | %.0f | %.2f | %.0f | %.0f |" % (n[:90], c, t, t / c, 100 * t / total, lo, hi))
+    expect = step_dispatches()
+    seqs, i = [], 0
+    while i < len(names):
+        j, ok, seq = i, True, []
+        for op, kernel in expect:
+            if j >= len(names) or names[j] != kernel:
+                ok = False
+                break
+            d = durs[j]
+            j += 1
+            while j < len(names) and names[j].startswith(SPLIT_KERNELS):
+                d += durs[j]
+                j += 1
+            seq.append(d)
+        if ok:
+            seqs.append(seq)
+            i = j
+        else:
+            i += 1
+    print()
+    print("%d complete step sequences in the trace.  Per op (mean over them):" % len(seqs))
+    print()
+    print("| Op | Kernel | Mean (us) |")
+    print("|---|---|---:|")
+    for k, (op, kernel) in enumerate(expect):
+        if seqs:
+            print("| %s | `%s` | %.1f |" % (op, kernel, sum(s[k] for s in seqs) / len(seqs) / 1e3))
 
 
 XCDS, SIMDS = 8, 1024          # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
@@ -270,6 +329,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=1536, help="rows per linear in the CPU-baseline sample")
     p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                    help="write profiles/hbm_traffic.json from two rocprofv3 counter databases (no GPU needed)")
+    p.add_argument("--trace-table", metavar="DB",
+                   help="print per-kernel and per-op tables from a rocprofv3 kernel-trace database (no GPU needed)")
     p.add_argument("--counter-table", nargs="+", metavar="DB",
                    help="print the step's per-dispatch counter table from rocprofv3 counter databases (no GPU needed)")
     return p.parse_args()
@@ -312,7 +373,7 @@ class Workload:
         """HIP kernel function an op launches (the GEMM kernels are templated on the epilogue)."""
         e = {"none": 0, "bias": 1, "bias_gelu": 2}[epi]
         if name.startswith("gemm_mxfp8"):
-            return "k_gemm_mxfp8<0, 0, %d, %s>" % (e, TILED_NAME)
+            return "k_gemm_mxfp8<0, 0, %d, %s, 1>" % (e, TILED_NAME)
         if name.startswith("gemm_nvfp4"):
             return "k_gemm_nvfp4<%d, false, true>" % e
         if name.startswith("quant_mxfp8"):
@@ -727,6 +788,9 @@ def cpu_baseline(rows_per_linear: int):
 
 def main():
     args = parse()
+    if args.trace_table:
+        trace_table(args.trace_table)
+        return
     if args.counter_table:
         counter_table(args.counter_table)
         return
@@ -867,11 +931,15 @@ def main():
         achieved = per_launch / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None}
+    # HBM bytes per launch from the committed counter record, over the same ops
     rec = measured_traffic(dom)
-    if rec is not None:
-        roofline["traffic"] = rec["bytes_per_launch"]
-        roofline["traffic_read"] = rec["read_bytes_per_launch"]
-        roofline["traffic_write"] = rec["write_bytes_per_launch"]
+    if rec is not None and all(op in rec["launches"] for op in d["ops"]):
+        got = [rec["launches"][op] for op in d["ops"]]
+        rd = sum(v["FETCH_SIZE_KiB"] for v in got) * 1024 * rec["scale"]["FETCH_SIZE"] / len(got)
+        wr = sum(v["WRITE_SIZE_KiB"] for v in got) * 1024 * rec["scale"]["WRITE_SIZE"] / len(got)
+        roofline["traffic"] = int(rd) + int(wr)
+        roofline["traffic_read"] = int(rd)
+        roofline["traffic_write"] = int(wr)
     roofline.update({"kernel": dom, "launches_per_step": d["launches1"] + len(d["excluded"]), "ops": d["ops"],
                      "ops_left_out": d["excluded"], "avg_launch_ms": round(avg_ms, 4),
                      "work_per_launch": per_launch, "work_unit": d["unit"]})
