@@ -19,7 +19,15 @@ timed region.  value = GEMM flops of the step / step time (TFLOP/s).  Per-op
 times come from HIP events on the launch stream around every launch.  The CPU
 oracle is timed on a bounded sample of the same work (cpu_baseline).
 
+Beside the step the line carries legs that are not part of it: measured_peaks
+(fp8 / fp16 matrix-core rates under load with the shader clock, a streaming
+copy), quantizer_only (cold / warm), long_sequence_chain (M = 32768, K = 4096),
+fusion_lower_bound, static_activation_scale, weight_only_fp8 and fp8_attention.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --trace-table DB            # summaries of rocprofv3 databases
+    python bench.py --record-traffic FETCH_DB WRITE_DB
+    python bench.py --counter-table DB [DB ...]
 """
 from __future__ import annotations
 
