@@ -228,12 +228,15 @@ mxq_status mxq_quantize_fp8_v(const void* v, int64_t heads, int64_t L, int64_t d
 /*
  * FP8 multi-head attention [P2 section 2.1: in the mixed-precision configuration,
  * multi-head attention runs in FP8], per head, non-causal:
- *   S = (s_q s_k / sqrt(d)) sum_c val(q[i,c]) val(k[j,c])
- *   online softmax over key blocks of 64 in key order: m' = max(m, max_j S_ij),
- *   P_ij = exp(S_ij - m'), l = l exp(m - m') + sum_j P_ij,
- *   acc = acc exp(m - m') + sum_j val(RN_E4M3(256 P_ij)) val(v[j,:])
- *   o[i,:] = bf16( s_v acc / (256 l) )
- * Both products on FP8 matrix cores with fp32 accumulation (exact products).
+ *   S_ij = (s_q s_k / sqrt(d)) sum_c val(q[i,c]) val(k[j,c])
+ *   m_i = max_j S_ij over every key of the row, P_ij = exp(S_ij - m_i),
+ *   l_i = sum_j P_ij (unquantized),
+ *   o[i,:] = bf16( s_v sum_j val(RN_E4M3(256 P_ij)) val(v[j,:]) / (256 l_i) )
+ * i.e. the probabilities enter the second product as E4M3 codes of 256 P,
+ * quantized against the row's own maximum (no blocking of the keys is part of
+ * the result).  Both products on FP8 matrix cores with fp32 accumulation (exact
+ * products); the kernel makes two passes over the keys (the maximum, then P and
+ * the product).
  *   q, k      : u8 [heads * L, d] E4M3 codes (mxq_quantize_fp8_weight with
  *               rows = heads * L), device; q_scale, k_scale their device fp32 scales.
  *   vt, v_scale: V in the layout of mxq_quantize_fp8_v, and its scale.
