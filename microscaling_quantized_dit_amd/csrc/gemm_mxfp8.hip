@@ -26,10 +26,11 @@
 // Each stage is split at a mid-stage barrier so that one
 // half's MFMAs overlap the other half's fragment reads and the DMA two stages
 // ahead; one dword of every row segment three stages ahead is loaded too, which
-// brings those cache lines into L2 before their DMA is issued.  The kernel is persistent (one workgroup per CU): a workgroup walks its
-// tiles as one stream of stages, so the next tile's first stages are in flight
-// during the previous tile's epilogue.  Tiles are ordered so that each XCD (one
-// L2) works on a contiguous range, in groups of four M-tiles.
+// brings those cache lines into L2 before their DMA is issued.  The kernel is
+// persistent (one workgroup per CU): a workgroup walks its tiles as one stream of
+// stages, so the next tile's first stages are in flight during the previous
+// tile's epilogue.  Tiles are ordered so that each XCD (one L2) works on a
+// contiguous range, in groups of eight M-tiles.
 #include <type_traits>
 
 #include "mxq_internal.h"
@@ -46,7 +47,7 @@ constexpr int kTile = 256;        // rows of W (n) and of A (m) per tile
 constexpr int kBK = 128;          // K bytes per stage = one LDS row
 constexpr int kOperand = kTile * kBK;          // 32 KiB
 constexpr int kStage = 2 * kOperand;           // W then A
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;
 constexpr int kCStage = dev::epilogue_lds_bytes(64);   // epilogue staging per wave
 // Mid-stage wait: every vector memory operation but the newest two (the stage's
 // L2 prefetch, issued right after its DMA) and every LDS read.  Vector memory
