@@ -285,6 +285,26 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
                           void* c, void* stream);
 
 /*
+ * MXFP8 GEMM with the activation quantizer fused into its prologue [P2 section 3.1:
+ * at run time the bf16 activation is quantized dynamically and handed with its
+ * scales to the low-precision GEMM; P1 MXFP8 paragraph].
+ *   C = epi( Q(a) . W^T ), Q the MXFP8 activation quantizer of mxq_quantize_mxfp8
+ *   in format kind.  The result is bit-identical to mxq_quantize_mxfp8(a, kind)
+ *   followed by mxq_gemm_mxfp8 with a_kind = w_kind = kind: the codes and scales
+ *   are the same, and so are the products, their accumulation order and the
+ *   epilogue.  A's codes never reach memory.
+ *   a          : bf16 [M, K] row-major, device.
+ *   kind       : element format of A's codes and of W (one format for both).
+ *   w_q, w_scales, scale_layout: W codes u8 [N, K] and E8M0 scales [N, K/32] in
+ *                scale_layout (from mxq_quantize_mxfp8).
+ *   M, N, K, bias, epi, c, errors: as mxq_gemm_mxfp8 (a counts 2 bytes per
+ *   element towards the 2 GiB operand limit).
+ */
+mxq_status mxq_gemm_mxfp8_fused(const void* a, mxq_fp8_kind kind, const void* w_q, const void* w_scales,
+                                mxq_scale_layout scale_layout, int64_t M, int64_t N, int64_t K,
+                                const void* bias, mxq_epilogue epi, void* c, void* stream);
+
+/*
  * Bytes of device workspace mxq_gemm_nvfp4 can use for this shape on the current
  * device (0 for an invalid shape).  With it, row-major block scales of both
  * operands are first rewritten into the tiled order (MXQ_SCALES_TILED; scales

@@ -37,7 +37,8 @@ _lib = None
 
 SYMBOLS = ["mxq_quantize_mxfp8", "mxq_quantize_nvfp4_workspace_size", "mxq_quantize_nvfp4",
            "mxq_quantize_nvfp4_noalloc",
-           "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_nvfp4_workspace_size",
+           "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight", "mxq_gemm_mxfp8", "mxq_gemm_mxfp8_fused",
+           "mxq_gemm_nvfp4_workspace_size",
            "mxq_gemm_nvfp4", "mxq_quantize_fp8_v", "mxq_attention_fp8",
            "mxq_gemm_bf16_fp8w", "mxq_status_string", "mxq_last_error"]
 
@@ -74,6 +75,7 @@ def load():
         lib.mxq_quantize_fp8_weight.argtypes = [P, i64, i64, P, P, P, P, sz, P]
         lib.mxq_gemm_bf16_fp8w.argtypes = [P, P, P, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_mxfp8.argtypes = [P, P, i32, P, P, i32, i32, i64, i64, i64, P, i32, P, P]
+        lib.mxq_gemm_mxfp8_fused.argtypes = [P, i32, P, P, i32, i64, i64, i64, P, i32, P, P]
         lib.mxq_gemm_nvfp4_workspace_size.argtypes = [i64, i64, i64]
         lib.mxq_gemm_nvfp4_workspace_size.restype = sz
         lib.mxq_gemm_nvfp4.argtypes = [P, P, P, P, P, P, i32, i64, i64, i64, P, i32, P, P, sz, P]
@@ -84,7 +86,8 @@ def load():
         lib.mxq_last_error.argtypes = []
         lib.mxq_last_error.restype = ctypes.c_char_p
         for f in ("mxq_quantize_mxfp8", "mxq_quantize_nvfp4", "mxq_quantize_nvfp4_noalloc", "mxq_nvfp4_calibrate", "mxq_quantize_fp8_weight",
-                  "mxq_gemm_mxfp8", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w", "mxq_quantize_fp8_v",
+                  "mxq_gemm_mxfp8", "mxq_gemm_mxfp8_fused", "mxq_gemm_nvfp4", "mxq_gemm_bf16_fp8w",
+                  "mxq_quantize_fp8_v",
                   "mxq_attention_fp8"):
             getattr(lib, f).restype = i32
         _lib = lib
@@ -314,6 +317,29 @@ def gemm_mxfp8(a_q, a_s, w_q, w_s, bias=None, epi=None, a_kind="e4m3", w_kind="e
         (c,) = _outputs(out, [("out", torch.bfloat16, (M, N))], a_q.device)
         _check(lib.mxq_gemm_mxfp8(_ptr(a_q), _ptr(a_s), _KIND[a_kind], _ptr(w_q), _ptr(w_s), _KIND[w_kind],
                                   _LAYOUT[scale_layout], M, N, K, _ptr(bias), e, _ptr(c), _stream(stream)))
+    return c
+
+
+def gemm_mxfp8_fused(a, w_q, w_s, kind="e4m3", bias=None, epi=None, out=None, stream=None, scale_layout="row"):
+    """C[M, N] = epi(Q(A) . W^T) in bf16: A bf16 [M, K] quantized to MXFP8 (format
+    kind) inside the GEMM, W MXFP8 [N, K] of the same format; bit-identical to
+    quantize_mxfp8 followed by gemm_mxfp8.  scale_layout names W's scale order."""
+    torch = _torch()
+    M, K = _x2d(a, "a")
+    if not isinstance(w_q, torch.Tensor) or w_q.dim() != 2:
+        raise ValueError("w_q must be a 2-D tensor")
+    N = w_q.shape[0]
+    _need(w_q, torch.uint8, "w_q", a.device, (N, K))
+    _need(w_s, torch.uint8, "w_s", a.device, (N, K // 32))
+    if epi is None:
+        epi = "none" if bias is None else "bias"
+    e = _epi(epi, bias)
+    _bias(bias, N, a.device)
+    lib = load()
+    with _on(stream):
+        (c,) = _outputs(out, [("out", torch.bfloat16, (M, N))], a.device)
+        _check(lib.mxq_gemm_mxfp8_fused(_ptr(a), _KIND[kind], _ptr(w_q), _ptr(w_s), _LAYOUT[scale_layout], M, N, K,
+                                        _ptr(bias), e, _ptr(c), _stream(stream)))
     return c
 
 

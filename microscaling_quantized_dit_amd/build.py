@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmxq.so")
 PROBES_LIB = os.path.join(PKG, "libmxq_probes.so")
 # the probes library also holds a probe build of the MXFP8 GEMM (MXQ_PROBE_BUILD)
 PROBES_SOURCES = ["probes.hip", "gemm_mxfp8.hip"]
-SOURCES = ["quant_mxfp8.hip", "quant_nvfp4.hip", "gemm_mxfp8.hip", "gemm_nvfp4.hip", "gemm_w8.hip", "gemm_fixup.hip",
+SOURCES = ["quant_mxfp8.hip", "quant_nvfp4.hip", "gemm_mxfp8.hip", "gemm_mxfp8_fused.hip", "gemm_nvfp4.hip", "gemm_w8.hip", "gemm_fixup.hip",
            "attention_fp8.hip", "mxq_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",

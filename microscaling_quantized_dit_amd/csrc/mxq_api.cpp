@@ -313,6 +313,24 @@ mxq_status mxq_gemm_mxfp8(const void* a_q, const void* a_scales, mxq_fp8_kind a_
                   "mxq_gemm_mxfp8 launch");
 }
 
+mxq_status mxq_gemm_mxfp8_fused(const void* a, mxq_fp8_kind kind, const void* w_q, const void* w_scales,
+                                mxq_scale_layout scale_layout, int64_t M, int64_t N, int64_t K, const void* bias,
+                                mxq_epilogue epi, void* c, void* stream) {
+  if (!a || !w_q || !w_scales) return fail(MXQ_ERROR_INVALID_VALUE, "null pointer argument");
+  if (kind != MXQ_FP8_E4M3 && kind != MXQ_FP8_E5M2) return fail(MXQ_ERROR_INVALID_VALUE, "bad fp8 kind");
+  if (scale_layout != MXQ_SCALES_ROW_MAJOR && scale_layout != MXQ_SCALES_TILED)
+    return fail(MXQ_ERROR_INVALID_VALUE, "bad scale layout %d", (int)scale_layout);
+  mxq_status s = check_gemm_common(M, N, K, bias, epi, c, 2, 1);
+  if (s != MXQ_SUCCESS) return s;
+  if (!aligned16(a) || !aligned16(w_q) || !aligned16(w_scales))
+    return fail(MXQ_ERROR_MISALIGNED, "operands must be 16-byte aligned");
+  mxq_status d = check_device();
+  if (d != MXQ_SUCCESS) return d;
+  return launched(mxq::launch_gemm_mxfp8_fused(a, (int)kind, w_q, w_scales, M, N, K, bias, (int)epi, c,
+                                               scale_layout == MXQ_SCALES_TILED, (hipStream_t)stream),
+                  "mxq_gemm_mxfp8_fused launch");
+}
+
 size_t mxq_gemm_nvfp4_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || M % 128 || N % 128 || K % 128) return 0;
   if (M >= kMax32 || N >= kMax32 || K >= kMax32) return 0;

@@ -85,6 +85,11 @@ hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const
                              const void* w_s, int w_kind, int64_t M, int64_t N, int64_t K,
                              const void* bias, int epi, void* c, bool scales_tiled, hipStream_t stream);
 
+// a: bf16 [M, K]; kind: A's code format and W's; scales_tiled: W's scale order
+hipError_t launch_gemm_mxfp8_fused(const void* a, int kind, const void* w_q, const void* w_s, int64_t M, int64_t N,
+                                   int64_t K, const void* bias, int epi, void* c, bool scales_tiled,
+                                   hipStream_t stream);
+
 // workspace: NULL (no split) or at least gemm_nvfp4_workspace_bytes(M, N, K) bytes
 size_t gemm_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_nvfp4(const void* a_q, const void* a_s, const float* a_g, const void* w_q,
@@ -152,6 +157,58 @@ __device__ __forceinline__ uint32_t mag_max_pk(uint4 v) {
 __device__ __forceinline__ uint32_t fold_halves_max(uint32_t pk) {
   uint32_t lo = pk & 0xFFFFu, hi = pk >> 16;
   return lo > hi ? lo : hi;
+}
+
+// MXFP8 element formats: E4M3 ("fn", largest finite 448 = 1.75 * 2^8) and E5M2
+// (largest finite 57344 = 1.75 * 2^15), with the hardware's round-to-nearest-even
+// pair conversion into the low (HI = false) or high half of a dword.
+template <int KIND>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<0> {
+  static constexpr int emax = 8;
+  static constexpr float maxval = 448.0f;
+  template <bool HI>
+  static __device__ __forceinline__ int cvt(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+  }
+};
+template <>
+struct Fp8Traits<1> {
+  static constexpr int emax = 15;
+  static constexpr float maxval = 57344.0f;
+  template <bool HI>
+  static __device__ __forceinline__ int cvt(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+  }
+};
+
+// MX block exponent E = floor(log2 amax) - emax, clamped to [-127, 127] (-127 for
+// an all-zero block), from the block's largest bf16 magnitude bits.  For a normal
+// amax floor(log2 amax) is its exponent field - 127; a subnormal (or zero) amax
+// has floor(log2) <= -127 and every emax is positive, so the clamp gives -127
+// whatever its mantissa: the exponent field alone decides.
+template <int KIND>
+__device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 7) - 127 - Fp8Traits<KIND>::emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four bf16 values (two dwords) times inv = 2^-E -> four fp8 codes.  x * 2^-E is
+// exact in fp32; the hardware conversion rounds to nearest even but turns
+// magnitudes at or above the saturation midpoint into NaN, so values are clamped
+// to the largest finite one first (which never changes an RNE result below the
+// clamp and yields the saturated code above it).
+template <int KIND>
+__device__ __forceinline__ int mx_encode4(uint32_t w0, uint32_t w1, float inv) {
+  using T = Fp8Traits<KIND>;
+  const float hi = T::maxval, lo = -T::maxval;
+  float f0 = __builtin_amdgcn_fmed3f(bf16_lo(w0) * inv, lo, hi);
+  float f1 = __builtin_amdgcn_fmed3f(bf16_hi(w0) * inv, lo, hi);
+  float f2 = __builtin_amdgcn_fmed3f(bf16_lo(w1) * inv, lo, hi);
+  float f3 = __builtin_amdgcn_fmed3f(bf16_hi(w1) * inv, lo, hi);
+  int r = T::template cvt<false>(f0, f1, 0);
+  return T::template cvt<true>(f2, f3, r);
 }
 
 // Two fp32 -> two bf16 (nearest, ties to even) packed low|high: v_cvt_pk_bf16_f32.

@@ -30,50 +30,6 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 2;  // 16-byte chunks per lane, kept in flight together
 constexpr int kUnrollTiled = 4;   // with tiled scales: 64 rows x 128 values per workgroup
 
-template <int KIND>
-struct Fp8Traits;
-template <>
-struct Fp8Traits<0> {  // E4M3 ("fn"): largest finite 448 = 1.75 * 2^8
-  static constexpr int emax = 8;
-  static constexpr float maxval = 448.0f;
-  template <bool HI>
-  static __device__ __forceinline__ int cvt(float a, float b, int old) {
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-  }
-};
-template <>
-struct Fp8Traits<1> {  // E5M2: largest finite 57344 = 1.75 * 2^15
-  static constexpr int emax = 15;
-  static constexpr float maxval = 57344.0f;
-  template <bool HI>
-  static __device__ __forceinline__ int cvt(float a, float b, int old) {
-    return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
-  }
-};
-
-// Shared exponent E from the block's largest bf16 magnitude bits.
-template <int KIND>
-__device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
-  if (amax_bits == 0) return -127;
-  uint32_t ef = amax_bits >> 7;
-  int fl = ef ? (int)ef - 127                          // normal: exponent field
-              : (31 - __clz((int)amax_bits)) - 133;    // subnormal: mant * 2^-133
-  int e = fl - Fp8Traits<KIND>::emax;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-template <int KIND>
-__device__ __forceinline__ int encode4(uint32_t w0, uint32_t w1, float inv) {
-  using T = Fp8Traits<KIND>;
-  const float hi = T::maxval, lo = -T::maxval;
-  float f0 = __builtin_amdgcn_fmed3f(dev::bf16_lo(w0) * inv, lo, hi);
-  float f1 = __builtin_amdgcn_fmed3f(dev::bf16_hi(w0) * inv, lo, hi);
-  float f2 = __builtin_amdgcn_fmed3f(dev::bf16_lo(w1) * inv, lo, hi);
-  float f3 = __builtin_amdgcn_fmed3f(dev::bf16_hi(w1) * inv, lo, hi);
-  int r = T::template cvt<false>(f0, f1, 0);
-  return T::template cvt<true>(f2, f3, r);
-}
-
 // TILED: scales in the GEMM-tiled order, with the work split of dev::TiledSlab
 // (every chunk in range); else the tensor is a flat stream of chunks.
 template <int KIND, bool TILED>
@@ -100,11 +56,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
     uint32_t m = dev::fold_halves_max(dev::mag_max_pk(v[u]));
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
-    const int E = block_exponent<KIND>(m);
+    const int E = dev::mx_block_exponent<KIND>(m);
     const float inv = __uint_as_float((uint32_t)(127 - E) << 23);  // 2^-E, normal
     uint2 out;
-    out.x = (uint32_t)encode4<KIND>(v[u].x, v[u].y, inv);
-    out.y = (uint32_t)encode4<KIND>(v[u].z, v[u].w, inv);
+    out.x = (uint32_t)dev::mx_encode4<KIND>(v[u].x, v[u].y, inv);
+    out.y = (uint32_t)dev::mx_encode4<KIND>(v[u].z, v[u].w, inv);
     if (TILED || c < n_chunks) {
       dev::store_nt(out, q + c);
       if ((t & 3) == 0) s[TILED ? ts.scale(u) : c >> 2] = (uint8_t)(E + 127);
