@@ -22,7 +22,7 @@ oracle is timed on a bounded sample of the same work (cpu_baseline).
 Beside the step the line carries legs that are not part of it: measured_peaks
 (fp8 / fp16 matrix-core rates under load with the shader clock, a streaming
 copy), quantizer_only (cold / warm), long_sequence_chain (M = 32768, K = 4096),
-fusion_lower_bound, static_activation_scale, weight_only_fp8 and fp8_attention.
+fused_quantize_gemm, static_activation_scale, weight_only_fp8 and fp8_attention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --trace-table DB            # summaries of rocprofv3 databases
@@ -671,6 +671,7 @@ def chain_long_sequence(torch, mxq, inputs, reps: int = 5):
         w = inputs.to_torch(inputs.weight(N, K, seed=0, stream="cfg5/W%d" % N), "cuda")
         b = inputs.to_torch(inputs.bias(N, K, seed=0, stream="cfg5/b%d" % N), "cuda")
         c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        cf = torch.empty_like(c)
         flops = 2 * M * N * K
         for fmt in ("e4m3", "e5m2", "nvfp4"):
             if fmt == "nvfp4":
@@ -707,48 +708,67 @@ def chain_long_sequence(torch, mxq, inputs, reps: int = 5):
             g_ms = _graph_time(torch, gemm, reps)
             t_ms = _graph_time(torch, lambda: (quant(), gemm()), reps)
             gemm_rate = flops / (g_ms * 1e-3) / 1e12
-            out["%s_N%d" % (fmt, N)] = {
+            rec = {
                 "quantize_ms": round(q_ms, 4), "quantize_GB/s": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
                 "gemm_ms": round(g_ms, 4), "gemm_TFLOP/s": round(gemm_rate, 1),
                 "gemm_frac_of_peak": round(gemm_rate / peak, 4), "peak_TFLOP/s": peak,
                 "chain_ms": round(t_ms, 4), "chain_TFLOP/s": round(flops / (t_ms * 1e-3) / 1e12, 1)}
-        del w, b, c
+            if fmt != "nvfp4":   # the same chain with the quantizer fused into the GEMM
+                def fused(fmt=fmt):
+                    mxq.gemm_mxfp8_fused(x, wq, ws_, kind=fmt, bias=b, epi="bias", out=cf, scale_layout=SCALES)
+                f_ms = _graph_time(torch, fused, reps)
+                quant(), gemm(), fused()
+                torch.cuda.synchronize()
+                rec["fused_ms"] = round(f_ms, 4)
+                rec["fused_bit_identical"] = bool(torch.equal(c.view(torch.int16), cf.view(torch.int16)))
+            out["%s_N%d" % (fmt, N)] = rec
+        del w, b, c, cf
     del x
     torch.cuda.synchronize()
     return out
 
 
-def fusion_lower_bound(torch, mxq, inputs, wl, reps: int = 20):
-    """Would fusing the activation quantizer into the MXFP8 GEMM's prologue pay on
-    the double-stream linears?  A fused kernel reads the bf16 activation (twice the
-    bytes of its codes) for every output tile column and quantizes it there.  A
-    lower bound of its time: the GEMM with every A stage DMA'd twice and no
-    quantization work at all (libmxq_probes.so).  Each sequence is one captured
-    graph replayed back to back (graph launch latency, alike in all, hides behind
-    the GEMM); fusion can save at most  separate - lower_bound, before paying for
-    quantizing each A tile once per output tile column and for an A stage twice
-    the size in LDS."""
+def fused_quantize_gemm(torch, mxq, inputs, wl, reps: int = 20):
+    """The activation quantizer fused into the MXFP8 GEMM's prologue
+    (mxq_gemm_mxfp8_fused, E4M3, the step's epilogues) against the separate
+    quantize + GEMM on the double-stream linears.  Beside them: the GEMM alone, and
+    a lower bound of any prologue fusion -- the GEMM with every A stage DMA'd twice
+    (the bf16-sized A traffic) and no quantization work (libmxq_probes.so).  Each
+    sequence is one captured graph replayed back to back; the fused output is
+    checked bit-identical to the separate one."""
     from microscaling_quantized_dit_amd import probes
-    out = {"probe": "k_gemm_mxfp8 with each A stage DMA'd twice (same bytes, same place)"}
+    out = {"lower_bound_probe": "k_gemm_mxfp8 with each A stage DMA'd twice (same bytes, same place)"}
     for L in wl.mx:
         c = torch.empty((M_MX, L["N"]), dtype=torch.bfloat16, device="cuda")
+        cf = torch.empty_like(c)
 
         def quant():
             mxq.quantize_mxfp8(L["x"], "e4m3", out=(L["aq"], L["as_"]), scale_layout=SCALES)
 
         def gemm():
-            mxq.gemm_mxfp8(L["aq"], L["as_"], L["wq"], L["ws"], out=c, scale_layout=SCALES)
+            mxq.gemm_mxfp8(L["aq"], L["as_"], L["wq"], L["ws"], bias=L["b"], epi=L["epi"], out=c,
+                           scale_layout=SCALES)
+
+        def fused():
+            mxq.gemm_mxfp8_fused(L["x"], L["wq"], L["ws"], kind="e4m3", bias=L["b"], epi=L["epi"], out=cf,
+                                 scale_layout=SCALES)
 
         def gemm2():
             probes.gemm_mxfp8_a_twice(L["aq"], L["as_"], L["wq"], L["ws"], c)
 
         sep = _graph_time(torch, lambda: (quant(), gemm()), reps)
         g_ms = _graph_time(torch, gemm, reps)
+        f_ms = _graph_time(torch, fused, reps)
         lb = _graph_time(torch, gemm2, reps)
+        quant(), gemm(), fused()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(c.view(torch.int16), cf.view(torch.int16)))
+        flops = 2 * M_MX * L["N"] * L["K"]
         out[L["name"]] = {"separate_quantize_then_gemm_ms": round(sep, 4), "gemm_ms": round(g_ms, 4),
-                          "fused_lower_bound_ms": round(lb, 4), "fusion_saves_at_most_ms": round(sep - lb, 4),
-                          "fusion_saves_at_most_frac": round((sep - lb) / sep, 4)}
-        del c
+                          "fused_ms": round(f_ms, 4), "fused_TFLOP/s": round(flops / (f_ms * 1e-3) / 1e12, 1),
+                          "fused_over_separate": round(f_ms / sep, 4), "fused_bit_identical": same,
+                          "a_twice_lower_bound_ms": round(lb, 4)}
+        del c, cf
     return out
 
 
@@ -998,7 +1018,7 @@ def main():
     print("bench: quantizer-only and long-sequence chain legs", file=sys.stderr, flush=True)
     result["quantizer_only"] = quantizer_only(torch, mxq, inputs, peaks["hbm_copy_GB/s"])
     result["long_sequence_chain"] = chain_long_sequence(torch, mxq, inputs)
-    result["fusion_lower_bound"] = fusion_lower_bound(torch, mxq, inputs, wl)
+    result["fused_quantize_gemm"] = fused_quantize_gemm(torch, mxq, inputs, wl)
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
     result["fp8_attention"] = fp8_attention_variant(torch, mxq, inputs)

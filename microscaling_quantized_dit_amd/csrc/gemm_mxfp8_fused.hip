@@ -50,6 +50,33 @@ constexpr int kCStage = dev::epilogue_lds_bytes(64);
 __device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
 
+// Four bf16 values (two dwords) -> four codes of x / 2^E, scale = 2^E: the
+// hardware's scaled conversion (v_cvt_scalef32_pk_fp8_bf16 / _bf8_bf16), which
+// divides by the scale exactly and rounds to nearest even -- the quantizer's
+// codes (mxq_internal.h mx_encode4) for every finite input below the saturation
+// midpoint (measured: every finite bf16 pattern under scales 2^-127 .. 2^127).
+// Above it the conversion gives NaN (E4M3: 0x7F) or infinity (E5M2: 0x7C) where
+// the quantizer clamps first; those codes are replaced by the largest finite one
+// (0x7E, 0x7B), sign kept: adding 1 (E4M3) or 4 (E5M2) to a code's magnitude
+// carries into bit 7 exactly for them.  Every magnitude reaching here is below
+// 2^(emax+1) x 2^E, where no other code can come out.
+template <int KIND>
+__device__ __forceinline__ uint32_t enc4_hw(uint32_t w0, uint32_t w1, float scale) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s r = {0, 0};
+  if constexpr (KIND == 0) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, w1), scale, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf, w0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf, w1), scale, true);
+  }
+  const uint32_t c = __builtin_bit_cast(uint32_t, r);
+  const uint32_t carry = KIND == 0 ? 0x01010101u : 0x04040404u;
+  return c - ((((c & 0x7F7F7F7Fu) + carry) & 0x80808080u) >> 7);
+}
+
 // Fragment of the 32x32x64 operand for this lane from a 64-byte fp8 row: the
 // 16-byte chunks g and g + 2 (K [16g, 16g+16) and [32+16g, 48+16g)).
 __device__ __forceinline__ v8i frag(const uint8_t* buf, int R, int g) {
@@ -158,15 +185,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8_fused(
       const uint32_t m = max(max(dev::fold_halves_max(dev::mag_max_pk(v[0])), dev::fold_halves_max(dev::mag_max_pk(v[1]))),
                              max(dev::fold_halves_max(dev::mag_max_pk(v[2])), dev::fold_halves_max(dev::mag_max_pk(v[3]))));
       const int E = dev::mx_block_exponent<KIND>(m);
-      const float inv = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E, normal
+      // 2^E as an fp32 (2^-127 is the subnormal 0x00400000)
+      const float scale = __uint_as_float(E > -127 ? (uint32_t)(E + 127) << 23 : 0x00400000u);
       e2 |= (uint32_t)(E + 127) << (8 * blk);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {   // 16 values -> one 16-byte chunk of codes
         uint4 o;
-        o.x = (uint32_t)dev::mx_encode4<KIND>(v[2 * h].x, v[2 * h].y, inv);
-        o.y = (uint32_t)dev::mx_encode4<KIND>(v[2 * h].z, v[2 * h].w, inv);
-        o.z = (uint32_t)dev::mx_encode4<KIND>(v[2 * h + 1].x, v[2 * h + 1].y, inv);
-        o.w = (uint32_t)dev::mx_encode4<KIND>(v[2 * h + 1].z, v[2 * h + 1].w, inv);
+        o.x = enc4_hw<KIND>(v[2 * h].x, v[2 * h].y, scale);
+        o.y = enc4_hw<KIND>(v[2 * h].z, v[2 * h].w, scale);
+        o.z = enc4_hw<KIND>(v[2 * h + 1].x, v[2 * h + 1].y, scale);
+        o.w = enc4_hw<KIND>(v[2 * h + 1].z, v[2 * h + 1].w, scale);
         *(uint4*)(qbuf + row * kRowQ + (((2 * blk + h) ^ xq) << 4)) = o;
       }
     }
@@ -212,6 +240,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8_fused(
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[i], fa[j], acc[i][j], KIND, KIND, 2 * HALF,
                                                                    (int)scw[i], 0, (int)sca[j]);
     quantize(an, qn, asn);
+    // the quantization's LDS reads first, then each MFMA followed by a share of its
+    // VALU work, its LDS writes last
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);
     __builtin_amdgcn_sched_barrier(0);
     // d) stage s+1's quantized A visible; its fragments
     __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);

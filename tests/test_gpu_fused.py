@@ -82,6 +82,34 @@ def test_fused_special_blocks(mxq):
     assert torch.isfinite(fused[128:160].float()).all().item()
 
 
+@pytest.mark.parametrize("kind", ["e4m3", "e5m2"])
+def test_fused_every_bf16_pattern(mxq, kind):
+    """Every finite bf16 pattern as an activation value, once in pattern order
+    (blocks of neighbouring magnitudes) and once in a seeded permutation (mixed
+    blocks), against the identity weight: C is then the dequantized activation
+    itself, so every code and block scale the fused kernel forms is compared with
+    the separate quantizer's (bit for bit) and with the oracle's (within the
+    GEMM tolerance; values below bf16's range underflow alike)."""
+    import torch
+    pats = np.arange(65536, dtype=np.uint32)
+    vals = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)          # 65280 finite patterns
+    rng = np.random.RandomState(5)
+    K = N = 512
+    a = np.concatenate([vals, vals[rng.permutation(vals.size)], np.zeros(K, np.uint16)]).reshape(-1, K)
+    eye = np.zeros((N, K), np.uint16)
+    eye[np.arange(N), np.arange(N)] = 0x3F80                              # 1.0
+    x, w = inputs.to_torch(a, "cuda"), inputs.to_torch(eye, "cuda")
+    for layout in ("row", "tiled"):
+        fused, chain = _chain_and_fused(mxq, x, w, kind, layout)
+        _assert_same(fused, chain, ("every pattern", kind, layout))
+    fmt = oracle.E4M3 if kind == "e4m3" else oracle.E5M2
+    aq, as_ = oracle.quantize_mxfp8(a, fmt)
+    wq, ws = oracle.quantize_mxfp8(eye, fmt)
+    r = oracle.gemm_mxfp8(aq, as_, wq, ws, fmt, fmt)
+    e = oracle.compare(_bf16(fused), r)
+    assert e["max_rel"] <= MAX_REL and e["fro_rel"] <= FRO_REL, (kind, e)
+
+
 @pytest.mark.parametrize("name,N,K,epi", [("qkv", 9216, 3072, "none"), ("out_proj", 3072, 3072, "none"),
                                           ("mlp_up", 12288, 3072, "bias_gelu"), ("mlp_down", 3072, 12288, "none")])
 def test_fused_flux_shapes(mxq, name, N, K, epi):
