@@ -18,6 +18,8 @@ int main(void) {
                                      192, NULL, MXQ_EPI_NONE, fake, NULL));
   printf("%d\n", (int)mxq_gemm_nvfp4(fake, fake, gs, fake, fake, gs, MXQ_SCALES_ROW_MAJOR, 128, 256, 256, NULL,
                                      MXQ_EPI_BIAS, fake, NULL, 0, NULL));
+  printf("%d\n", (int)mxq_gemm_mxfp8_fused(fake, MXQ_FP8_E5M2, fake, fake, MXQ_SCALES_TILED, 128, 256, 192, NULL,
+                                           MXQ_EPI_NONE, fake, NULL));
   printf("%zu\n", mxq_gemm_nvfp4_workspace_size(128, 384, 128));
   printf("%zu\n", mxq_quantize_nvfp4_workspace_size(128, 24));
   printf("%s\n", mxq_status_string(MXQ_ERROR_MISALIGNED));

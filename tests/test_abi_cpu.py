@@ -185,6 +185,22 @@ def test_gemm_mxfp8_validation(lib):
     assert _g8(lib, layout=TILED, K=192) == SHAPE
 
 
+def test_gemm_mxfp8_fused_validation(lib):
+    def call(a=FAKE, kind=0, w=FAKE2, ws=FAKE, layout=ROW, M=128, N=256, K=256, bias=None, epi=0, c=FAKE):
+        return lib.mxq_gemm_mxfp8_fused(a, kind, w, ws, layout, M, N, K, bias, epi, c, None)
+
+    assert call(a=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(kind=2) == INVALID
+    assert call(layout=3) == INVALID
+    assert call(epi=1) == INVALID                    # bias required
+    assert call(K=192) == SHAPE
+    assert call(M=1 << 20, K=1024) == SHAPE          # A > 2 GiB at 2 bytes per element
+    assert call(a=MIS) == MISALIGNED
+    assert call(ws=MIS) == MISALIGNED
+    assert call() == DEVICE                          # valid arguments, no GPU here
+
+
 def test_gemm_nvfp4_validation(lib):
     def call(M=128, N=256, K=256, ag=FAKE, bias=None, epi=0, c=FAKE, ws=None, nbytes=0, layout=ROW):
         return lib.mxq_gemm_nvfp4(FAKE, FAKE2, ag, FAKE, FAKE2, FAKE, layout, M, N, K, bias, epi, c, ws, nbytes,

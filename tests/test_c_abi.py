@@ -29,8 +29,8 @@ def test_c99_client_compiles_links_and_validates(tmp_path):
     env["LD_LIBRARY_PATH"] = os.pathsep.join(p for p in ["/opt/rocm/lib", env.get("LD_LIBRARY_PATH", "")] if p)
     out = subprocess.run([str(exe)], check=True, capture_output=True, text=True, env=env, timeout=120).stdout
     lines = out.split("\n")
-    assert [int(x) for x in lines[:6]] == [INVALID, SHAPE, SHAPE, SHAPE, SHAPE, INVALID]
-    assert int(lines[6]) == 128 * 8 + 384 * 8      # both operands' re-laid scales, no split
-    assert int(lines[7]) == 0                      # cols not a multiple of 16
-    assert "misaligned" in lines[8]
-    assert lines[9] == "1"                         # the last failure left its detail
+    assert [int(x) for x in lines[:7]] == [INVALID, SHAPE, SHAPE, SHAPE, SHAPE, INVALID, SHAPE]
+    assert int(lines[7]) == 128 * 8 + 384 * 8      # both operands' re-laid scales, no split
+    assert int(lines[8]) == 0                      # cols not a multiple of 16
+    assert "misaligned" in lines[9]
+    assert lines[10] == "1"                        # the last failure left its detail
