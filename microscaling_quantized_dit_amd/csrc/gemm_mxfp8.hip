@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
                                         m0 + wm * 128, n0 + wn * 128, lane);
   };
 
-  // One stage (buffer cur holds it; nxt holds the next one, possibly of the next tile):
+  // One stage (buffer cur holds it; nxt holds the next one, possibly of the next
+  // tile) is phase_a, then phase_bc:
   //   A: MFMAs of half 0 (registers) || LDS reads of half 1 of this stage
   //   B: wait for the next stage's DMA and this wave's reads, barrier (cur is now
   //      free in every wave, the next stage visible in nxt).  The wait depends on
@@ -217,9 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   //   C: MFMAs of half 1 || LDS reads of half 0 and the scales of the next stage;
   //      DMA of the stage after next (given by dm0, dn0, dk0, dvalid) into cur,
   //      then the L2 prefetch of the stage after that (pm0, pn0, pk0, pvalid).
-  auto stage = [&](auto kind_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
-                   int dm0, int dn0, int dk0, bool dvalid, int pm0, int pn0, int pk0, bool pvalid) {
-    // ---- A
+  auto phase_a = [&](v16f (&acc)[4][4], const uint8_t* cur) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f1w[i] = frag(cur, wrow + 32 * i, x, 1, g);
@@ -237,13 +236,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
-    // ---- B
+  };
+  auto phase_bc = [&](auto kind_, v16f (&acc)[4][4], uint8_t* cur, uint8_t* nxt, uint32_t* scur, uint32_t* snxt,
+                      int dm0, int dn0, int dk0, bool dvalid, int pm0, int pn0, int pk0, bool pvalid) {
     constexpr int kind = decltype(kind_)::value;
     if constexpr (kind == 0) __builtin_amdgcn_s_waitcnt(dev::kWaitLgkm);
     else if constexpr (kind == 1) __builtin_amdgcn_s_waitcnt(dev::kWaitAll);
     else __builtin_amdgcn_s_waitcnt(kWaitDmaLeavePrefetch);
     dev::lds_barrier();
-    // ---- C
     read_scales(snxt);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -276,7 +276,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   origin(0, m0, n0);
   if (my_tiles > 1) origin(1, m0n, n0n);
 
-  // Prologue: the first two stages in flight; wait; stage 0's scales and first-half fragments.
+  // Prologue: the first two stages in flight; wait (each tile reads its first
+  // stage's scales and first-half fragments at its top).
   {
     const bool nx1 = nk < 2;
     dma_stage(lds0, sc0, m0, n0, 0, true);
@@ -284,14 +285,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   }
   __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
   dev::lds_barrier();
-  read_scales(sc0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f0w[i] = frag(lds0, wrow + 32 * i, x, 0, g);
-    f0a[i] = frag(lds0 + kOperand, arow + 32 * i, x, 0, g);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
 
   // Global stage g uses buffer g & 1.  With an even number of stages per tile every
   // tile starts in buffer 0; with an odd number the launcher gives each workgroup a
@@ -304,6 +297,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
   for (int ti = 0; ti < my_tiles; ++ti) {
     lane_setup(true);
     const bool has_next = ti + 1 < my_tiles;
+    // the tile's first stage, visible in lds0 since the previous stage's barrier:
+    // its scales and first-half fragments (read here rather than carried across the
+    // previous tile's epilogue)
+    read_scales(sc0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f0w[i] = frag(lds0, wrow + 32 * i, x, 0, g);
+      f0a[i] = frag(lds0 + kOperand, arow + 32 * i, x, 0, g);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { scw[i] = nscw[i] >> (8 * g); sca[i] = nsca[i] >> (8 * g); }
     v16f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -311,24 +315,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mxfp8(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    auto one = [&](auto kind_, uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
+    auto bc = [&](auto kind_, uint8_t* c0, uint8_t* c1, uint32_t* t0, uint32_t* t1, int kt) {
       const int kk = kt + 2, kp = kt + 3;
       const bool nx = kk >= nk, nxp = kp >= nk;
-      stage(kind_, acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK, !nx || has_next,
-            nxp ? m0n : m0, nxp ? n0n : n0, (nxp ? kp - nk : kp) * kBK, !nxp || has_next);
+      phase_bc(kind_, acc, c0, c1, t0, t1, nx ? m0n : m0, nx ? n0n : n0, (nx ? kk - nk : kk) * kBK,
+               !nx || has_next, nxp ? m0n : m0, nxp ? n0n : n0, (nxp ? kp - nk : kp) * kBK, !nxp || has_next);
     };
-    one(First(), lds0, lds1, sc0, sc1, 0);
-    // the tile's bias, read by this wave's epilogue from LDS, so that no global load
-    // there queues behind the epilogue's own stores (issued after the first stage:
-    // its reads then need not wait for it)
+    phase_a(acc, lds0);
+    bc(First(), lds0, lds1, sc0, sc1, 0);
     if constexpr (EPI >= 1) dev::load_bias(rb, bias_lds + wave * 1024, n0 + wn * 128, lane);
-    if (nk > 1) one(Second(), lds1, lds0, sc1, sc0, 1);
-    int kt = 2;
-    for (; kt + 1 < nk; kt += 2) {
-      one(Later(), lds0, lds1, sc0, sc1, kt);
-      one(Later(), lds1, lds0, sc1, sc0, kt + 1);
+    if (nk > 1) {
+      phase_a(acc, lds1);
+      bc(Second(), lds1, lds0, sc1, sc0, 1);
     }
-    if (kt < nk) one(Later(), lds0, lds1, sc0, sc1, kt);
+    // The loop is rotated so that its header sits right before a stage's full wait:
+    // every wait the compiler derives inside the body is then exact.
+    int kt = 2;
+    if (kt < nk) {
+      phase_a(acc, lds0);
+      for (; kt + 2 < nk; kt += 2) {
+        bc(Later(), lds0, lds1, sc0, sc1, kt);
+        phase_a(acc, lds1);
+        bc(Later(), lds1, lds0, sc1, sc0, kt + 1);
+        phase_a(acc, lds0);
+      }
+      bc(Later(), lds0, lds1, sc0, sc1, kt);
+      if (kt + 1 < nk) {
+        phase_a(acc, lds1);
+        bc(Later(), lds1, lds0, sc1, sc0, kt + 1);
+      }
+    }
     // Retire the next tile's first two stages of DMA now: the stores below share
     // the counter, and the next tile's first stage then waits for none of them.
     __builtin_amdgcn_s_waitcnt(dev::kWaitVm);
@@ -381,7 +397,6 @@ hipError_t launch_gemm_mxfp8_a_twice(const void* a_q, const void* a_s, const voi
   return hipGetLastError();
 }
 #endif
-
 // Shapes reaching here are validated: M, N, K positive multiples of 128, kinds 0/1, epi 0..2.
 // Partial 256-tiles (M or N = 128 mod 256) skip the stores of their missing half.
 hipError_t launch_gemm_mxfp8(const void* a_q, const void* a_s, int a_kind, const void* w_q, const void* w_s,
