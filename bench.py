@@ -34,6 +34,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import statistics
 import os
 import sys
 import time
@@ -444,14 +445,13 @@ class Workload:
         return w
 
 
-def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
+def static_scale_variant(torch, mxq, inputs, wl):
     """The single-stream NVFP4 activation quantizers with a static, calibrated
     decode scale instead of the dynamic one: calibration folds two synthetic
     activations per linear (the step's recipe, other seeds, 4608 rows) into the
     scale on the GPU; then the static (one-pass) and dynamic (two-pass)
-    quantizers are timed back to back on the step's activation."""
+    quantizers are timed in alternating rounds on the step's activation."""
     out = {"calibration": "2 synthetic activations per linear (4608 rows each, same recipe, other seeds)"}
-    stream = torch.cuda.current_stream()
     for L in wl.nv:
         running = None
         for i in range(2):
@@ -467,17 +467,7 @@ def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
         def run_dynamic():
             mxq.quantize_nvfp4(L["x"], out=(L["aq"], L["as_"], g), workspace=L["wsb"], scale_layout=SCALES)
 
-        res = {}
-        for tag, f in (("static", run_static), ("dynamic", run_dynamic)):
-            for _ in range(3):
-                f()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                f()
-            b.record(stream)
-            torch.cuda.synchronize()
-            res[tag] = a.elapsed_time(b) / reps
+        res = _interleaved_ms(torch, {"static": run_static, "dynamic": run_dynamic})
         n = M_NV * L["K"]
         nbytes = 2 * n + n // 2 + n // 16 + 4
         rate = nbytes / (res["static"] * 1e-3) / 1e9
@@ -488,35 +478,46 @@ def static_scale_variant(torch, mxq, inputs, wl, reps: int = 20):
     return out
 
 
-def weight_only_fp8_variant(torch, mxq, inputs, wl, reps: int = 20):
+def _interleaved_ms(torch, fns, rounds: int = 15, inner: int = 5):
+    """Median ms per call of each function in `fns` (name -> callable), timed in
+    alternating rounds of `inner` back-to-back calls each (events on the current
+    stream), so that clock and thermal drift during the measurement fall on all of
+    them alike.  Each function is called three times first."""
+    stream = torch.cuda.current_stream()
+    for f in fns.values():
+        for _ in range(3):
+            f()
+    times = {k: [] for k in fns}
+    for _ in range(rounds):
+        for k, f in fns.items():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(inner):
+                f()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times[k].append(a.elapsed_time(b) / inner)
+    return {k: statistics.median(v) for k, v in times.items()}
+
+
+def weight_only_fp8_variant(torch, mxq, inputs, wl):
     """Weight-only FP8 on the double-stream linears: per-tensor E4M3 weights (quantized
     once, timed separately), the step's bf16 activations taken as they are, the same
     epilogues.  torch's bf16 GEMM on the same shapes is timed beside it for context."""
     out = {"weights": "per-tensor E4M3, dynamic scale from the weight's amax",
-           "peak_TFLOP/s": PEAK_BF16_TFLOPS}
-    stream = torch.cuda.current_stream()
-
-    def timed(f):
-        for _ in range(3):
-            f()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            f()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
+           "peak_TFLOP/s": PEAK_BF16_TFLOPS, "timing": "ours and torch's in alternating rounds, medians"}
     for L in wl.mx:
         w = inputs.to_torch(inputs.weight(L["N"], L["K"], seed=0, stream="bench/%s/W" % L["name"]), "cuda")
-        q_ms = timed(lambda: mxq.quantize_fp8_weight(w))
         wq, ws = mxq.quantize_fp8_weight(w)
         c = torch.empty((M_MX, L["N"]), dtype=torch.bfloat16, device="cuda")
-        g_ms = timed(lambda: mxq.gemm_bf16_fp8w(L["x"], wq, ws, bias=L["b"], epi=L["epi"], out=c))
         if L["epi"] == "bias_gelu":   # torch's bf16 GEMM with the same epilogue
-            t_ms = timed(lambda: torch.nn.functional.gelu(torch.addmm(L["b"], L["x"], w.t()), approximate="tanh"))
+            ref = lambda: torch.nn.functional.gelu(torch.addmm(L["b"], L["x"], w.t()), approximate="tanh")
         else:
-            t_ms = timed(lambda: torch.matmul(L["x"], w.t()))
+            ref = lambda: torch.matmul(L["x"], w.t())
+        ms = _interleaved_ms(torch, {"ours": lambda: mxq.gemm_bf16_fp8w(L["x"], wq, ws, bias=L["b"], epi=L["epi"],
+                                                                        out=c),
+                                     "torch": ref, "quantize": lambda: mxq.quantize_fp8_weight(w)})
+        g_ms, t_ms, q_ms = ms["ours"], ms["torch"], ms["quantize"]
         flops = 2 * M_MX * L["N"] * L["K"]
         rate = flops / (g_ms * 1e-3) / 1e12
         out["gemm_bf16_fp8w_" + L["name"]] = {
@@ -528,7 +529,7 @@ def weight_only_fp8_variant(torch, mxq, inputs, wl, reps: int = 20):
     return out
 
 
-def fp8_attention_variant(torch, mxq, inputs, reps: int = 20):
+def fp8_attention_variant(torch, mxq, inputs):
     """FP8 multi-head attention at FLUX's joint attention shape (24 heads of 128
     over 4608 tokens): per-tensor E4M3 quantization of Q, K and V (timed apart),
     then the attention kernel; torch's bf16 scaled_dot_product_attention on the
@@ -536,27 +537,16 @@ def fp8_attention_variant(torch, mxq, inputs, reps: int = 20):
     heads, L, d = 24, 4608, 128
     qb, kb, vb = inputs.attention_qkv(heads, L, d, seed=0, stream="bench/attn")
     q, k, v = (inputs.to_torch(x, "cuda") for x in (qb, kb, vb))
-    stream = torch.cuda.current_stream()
-
-    def timed(f):
-        for _ in range(3):
-            f()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            f()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
     qc, qs = mxq.quantize_fp8_weight(q)
     kc, ks = mxq.quantize_fp8_weight(k)
     vc, vs = mxq.quantize_fp8_v(v, heads)
     o = torch.empty((heads * L, d), dtype=torch.bfloat16, device="cuda")
-    a_ms = timed(lambda: mxq.attention_fp8(qc, qs, kc, ks, vc, vs, heads, out=o))
-    q_ms = timed(lambda: (mxq.quantize_fp8_weight(q), mxq.quantize_fp8_weight(k), mxq.quantize_fp8_v(v, heads)))
     q4, k4, v4 = (x.view(1, heads, L, d) for x in (q, k, v))
-    t_ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q4, k4, v4))
+    ms = _interleaved_ms(torch, {
+        "attention": lambda: mxq.attention_fp8(qc, qs, kc, ks, vc, vs, heads, out=o),
+        "quantize": lambda: (mxq.quantize_fp8_weight(q), mxq.quantize_fp8_weight(k), mxq.quantize_fp8_v(v, heads)),
+        "torch": lambda: torch.nn.functional.scaled_dot_product_attention(q4, k4, v4)})
+    a_ms, q_ms, t_ms = ms["attention"], ms["quantize"], ms["torch"]
     flops = 4 * heads * L * L * d
     rate = flops / (a_ms * 1e-3) / 1e12
     return {"shape": {"heads": heads, "tokens": L, "head_dim": d}, "flops": flops, "ms": round(a_ms, 4),
