@@ -186,6 +186,34 @@ def test_more_tiles_than_compute_units(mxq, K):
     _assert_close(*run_nv(mxq, NV(a), NV(w), bias=b, epi="bias"), "nv K=%d" % K)
 
 
+@pytest.mark.parametrize("K", [256, 512])
+@pytest.mark.parametrize("kind,layout", [("e4m3", "row"), ("e5m2", "row"), ("e4m3", "tiled")])
+def test_mxfp8_persistent_equals_row_slices(mxq, K, kind, layout):
+    """288 tiles (more than the compute units) with two or four K stages each: the
+    persistent launch, whose DMA runs into the next tile, must give the same bits
+    as the GEMM done on 256-row slices of A (18 tiles per launch, one tile per
+    workgroup), with bias, in three repetitions.  The codes come from the GPU
+    quantizer; only the two launch forms are compared."""
+    import torch
+    M, N = 4096, 4608
+    x = inputs.to_torch(inputs.flux_activation(M, K, seed=K, stream="persist/A"), "cuda")
+    w = inputs.to_torch(inputs.weight(N, K, seed=K, stream="persist/W"), "cuda")
+    b = inputs.to_torch(inputs.bias(N, K, seed=K, stream="persist/b"), "cuda")
+    aq, as_ = mxq.quantize_mxfp8(x, kind, scale_layout="row")
+    wq, ws = mxq.quantize_mxfp8(w, kind, scale_layout=layout)
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, M, 256):   # row-major scales slice with the rows
+        sa, ss = mxq.quantize_mxfp8(x[r0:r0 + 256], kind, scale_layout=layout)
+        ref[r0:r0 + 256] = mxq.gemm_mxfp8(sa, ss, wq, ws, bias=b, epi="bias", a_kind=kind, w_kind=kind,
+                                          scale_layout=layout)
+    if layout == "tiled":
+        aq, as_ = mxq.quantize_mxfp8(x, kind, scale_layout="tiled")
+    for rep in range(3):
+        c = mxq.gemm_mxfp8(aq, as_, wq, ws, bias=b, epi="bias", a_kind=kind, w_kind=kind, scale_layout=layout)
+        same = torch.eq(c.view(torch.int16), ref.view(torch.int16))
+        assert bool(same.all().item()), (K, kind, layout, rep, int((~same).sum().item()))
+
+
 @pytest.mark.parametrize("M,N,K", [(384, 640, 256), (640, 384, 1152), (4096, 4096, 1024), (128, 128, 128)])
 def test_nvfp4_scale_layouts_agree(mxq, M, N, K):
     """Given a workspace, the NVFP4 GEMM first re-lays both operands' block scales
