@@ -214,6 +214,33 @@ def test_mxfp8_persistent_equals_row_slices(mxq, K, kind, layout):
         assert bool(same.all().item()), (K, kind, layout, rep, int((~same).sum().item()))
 
 
+@pytest.mark.parametrize("K", [256, 512])
+def test_nvfp4_and_w8_persistent_equal_row_slices(mxq, K):
+    """As for MXFP8: the persistent NVFP4 GEMM (whole tiles only, split=False) and
+    the weight-only FP8 GEMM over 288 tiles give the same bits as on 256-row slices
+    of A (one tile per workgroup), with bias, in two repetitions."""
+    import torch
+    M, N = 4096, 4608
+    x = inputs.to_torch(inputs.flux_activation(M, K, seed=K + 1, stream="persist/A"), "cuda")
+    w = inputs.to_torch(inputs.weight(N, K, seed=K + 1, stream="persist/W"), "cuda")
+    b = inputs.to_torch(inputs.bias(N, K, seed=K + 1, stream="persist/b"), "cuda")
+    aq, as_, ag = mxq.quantize_nvfp4(x)
+    wq, ws, wg = mxq.quantize_nvfp4(w)
+    w8q, w8s = mxq.quantize_fp8_weight(w)
+    ref_nv = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ref_w8 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, M, 256):
+        ref_nv[r0:r0 + 256] = mxq.gemm_nvfp4(aq[r0:r0 + 256].contiguous(), as_[r0:r0 + 256].contiguous(), ag, wq, ws, wg,
+                                             bias=b, epi="bias_gelu", split=False)
+        ref_w8[r0:r0 + 256] = mxq.gemm_bf16_fp8w(x[r0:r0 + 256].contiguous(), w8q, w8s, bias=b, epi="bias_gelu")
+    for rep in range(2):
+        c_nv = mxq.gemm_nvfp4(aq, as_, ag, wq, ws, wg, bias=b, epi="bias_gelu", split=False)
+        c_w8 = mxq.gemm_bf16_fp8w(x, w8q, w8s, bias=b, epi="bias_gelu")
+        for c, ref, what in ((c_nv, ref_nv, "nvfp4"), (c_w8, ref_w8, "w8")):
+            same = torch.eq(c.view(torch.int16), ref.view(torch.int16))
+            assert bool(same.all().item()), (what, K, rep, int((~same).sum().item()))
+
+
 @pytest.mark.parametrize("M,N,K", [(384, 640, 256), (640, 384, 1152), (4096, 4096, 1024), (128, 128, 128)])
 def test_nvfp4_scale_layouts_agree(mxq, M, N, K):
     """Given a workspace, the NVFP4 GEMM first re-lays both operands' block scales
