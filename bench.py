@@ -529,6 +529,66 @@ def weight_only_fp8_variant(torch, mxq, inputs, wl):
     return out
 
 
+def torch_mxfp8_gemm(torch, mxq, inputs, wl):
+    """torch's own MXFP8 GEMM beside ours, on the same E4M3 codes and E8M0 scales:
+    torch.nn.functional.scaled_mm with one scale per 32 K-values on both operands
+    (row-major scales, no swizzle; ROCm builds run it on hipBLASLt), against
+    mxq_gemm_mxfp8 with the scales in the row-major and in the tiled order.  No
+    epilogue on either side (torch's call fuses no GELU).  Shapes: the step's
+    double-stream linears and the long-sequence ones (32768 tokens, K = 4096).
+    deviation: |torch - ours| over the whole output, relative to ours (Frobenius),
+    and its largest element relative to max |ours|."""
+    F = torch.nn.functional
+    if not hasattr(F, "scaled_mm") or not hasattr(torch, "float8_e8m0fnu"):
+        return {"error": "this torch has no scaled_mm with E8M0 scales"}
+    out = {"call": "torch.nn.functional.scaled_mm, ScalingType.BlockWise1x32 on both operands, bf16 out",
+           "timing": "alternating rounds, medians", "peak_TFLOP/s": PEAK_TFLOPS["fp8"]}
+    shapes = [(L["name"], M_MX, L["N"], L["K"], L["x"], "bench/%s/W" % L["name"]) for L in wl.mx]
+    xl = inputs.to_torch(inputs.long_sequence_activation(32768, 4096, seed=0, stream="cfg5/A"), "cuda")
+    shapes += [("long_sequence_n%d" % n, 32768, n, 4096, xl, "cfg5/W%d" % n) for n in (4096, 16384)]
+    for name, M, N, K, x, wstream in shapes:
+        w = inputs.to_torch(inputs.weight(N, K, seed=0, stream=wstream), "cuda")
+        aq, as_ = mxq.quantize_mxfp8(x, "e4m3")
+        wq, ws = mxq.quantize_mxfp8(w, "e4m3")
+        aqt, ast = mxq.quantize_mxfp8(x, "e4m3", scale_layout="tiled")
+        wqt, wst = mxq.quantize_mxfp8(w, "e4m3", scale_layout="tiled")
+        c_row = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        c_tiled = torch.empty_like(c_row)
+        a8, b8 = aq.view(torch.float8_e4m3fn), wq.view(torch.float8_e4m3fn).t()
+        sa, sb = as_.view(torch.float8_e8m0fnu), ws.view(torch.float8_e8m0fnu)
+
+        def theirs():
+            return F.scaled_mm(a8, b8, sa, F.ScalingType.BlockWise1x32, sb, F.ScalingType.BlockWise1x32,
+                               swizzle_a=F.SwizzleType.NO_SWIZZLE, swizzle_b=F.SwizzleType.NO_SWIZZLE,
+                               output_dtype=torch.bfloat16)
+        try:
+            ref = theirs()
+            torch.cuda.synchronize()
+        except Exception as e:      # a torch build without this path: say so, keep the rest of the line
+            out[name] = {"error": "%s: %s" % (type(e).__name__, str(e).splitlines()[0][:200])}
+            continue
+        mine = mxq.gemm_mxfp8(aqt, ast, wqt, wst, out=c_tiled, scale_layout="tiled")
+        d = (ref.float() - mine.float())
+        mf = mine.float()
+        dev = {"fro_rel": round((d.norm() / mf.norm()).item(), 6),
+               "max_rel": round((d.abs().max() / mf.abs().max()).item(), 6)}
+        ms = _interleaved_ms(torch, {
+            "tiled": lambda: mxq.gemm_mxfp8(aqt, ast, wqt, wst, out=c_tiled, scale_layout="tiled"),
+            "row": lambda: mxq.gemm_mxfp8(aq, as_, wq, ws, out=c_row),
+            "torch": theirs})
+        flops = 2 * M * N * K
+        tf = lambda k: round(flops / (ms[k] * 1e-3) / 1e12, 1)
+        out[name] = {"shape": [M, N, K], "ms": round(ms["tiled"], 4), "TFLOP/s": tf("tiled"),
+                     "ms_row_scales": round(ms["row"], 4), "TFLOP/s_row_scales": tf("row"),
+                     "torch_ms": round(ms["torch"], 4), "torch_TFLOP/s": tf("torch"),
+                     "speedup_vs_torch": round(ms["torch"] / ms["tiled"], 3),
+                     "speedup_vs_torch_row_scales": round(ms["torch"] / ms["row"], 3), "deviation": dev}
+        del w, aq, as_, wq, ws, aqt, ast, wqt, wst, c_row, c_tiled, ref, mine, d, mf
+    del xl
+    torch.cuda.empty_cache()
+    return out
+
+
 def fp8_attention_variant(torch, mxq, inputs):
     """FP8 multi-head attention at FLUX's joint attention shape (24 heads of 128
     over 4608 tokens): per-tensor E4M3 quantization of Q, K and V (timed apart),
@@ -1009,6 +1069,8 @@ def main():
     result["quantizer_only"] = quantizer_only(torch, mxq, inputs, peaks["hbm_copy_GB/s"])
     result["long_sequence_chain"] = chain_long_sequence(torch, mxq, inputs)
     result["fused_quantize_gemm"] = fused_quantize_gemm(torch, mxq, inputs, wl)
+    print("bench: torch's MXFP8 GEMM on the same operands", file=sys.stderr, flush=True)
+    result["torch_mxfp8_gemm"] = torch_mxfp8_gemm(torch, mxq, inputs, wl)
     result["static_activation_scale"] = static_scale_variant(torch, mxq, inputs, wl)
     result["weight_only_fp8"] = weight_only_fp8_variant(torch, mxq, inputs, wl)
     result["fp8_attention"] = fp8_attention_variant(torch, mxq, inputs)
