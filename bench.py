@@ -22,7 +22,8 @@ oracle is timed on a bounded sample of the same work (cpu_baseline).
 Beside the step the line carries legs that are not part of it: measured_peaks
 (fp8 / fp16 matrix-core rates under load with the shader clock, a streaming
 copy), quantizer_only (cold / warm), long_sequence_chain (M = 32768, K = 4096),
-fused_quantize_gemm, static_activation_scale, weight_only_fp8 and fp8_attention.
+fused_quantize_gemm, torch_mxfp8_gemm (torch's own MXFP8 GEMM on the same
+operands), static_activation_scale, weight_only_fp8 and fp8_attention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --trace-table DB            # summaries of rocprofv3 databases
