@@ -10,7 +10,10 @@
 //
 // HBM-bound, one pass.  The tensor is treated as a flat stream (cols % 32 == 0,
 // so blocks never straddle rows and the scale of element e is scales[e / 32]),
-// read and written with streaming (nt) accesses: each byte is touched once.
+// read with streaming (nt) loads, each input byte being touched once.  The codes
+// go out with ordinary stores: the GEMM reads them next, and codes left in the
+// caches spare its first touch of HBM (the quantizer and the GEMM after a cache
+// flush ran 0.5-6% faster together than with streaming stores).
 // Scales go out row-major or in the GEMM-tiled order (mxq_internal.h); for the
 // latter a workgroup takes 64 rows x 128 values, four rows per wave, so that
 // each wave's scale bytes form one contiguous run.
@@ -62,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_mxfp8(const uint4* __restric
     out.x = (uint32_t)dev::mx_encode4<KIND>(v[u].x, v[u].y, inv);
     out.y = (uint32_t)dev::mx_encode4<KIND>(v[u].z, v[u].w, inv);
     if (TILED || c < n_chunks) {
-      dev::store_nt(out, q + c);
+      q[c] = out;
       if ((t & 3) == 0) s[TILED ? ts.scale(u) : c >> 2] = (uint8_t)(E + 127);
     }
   }

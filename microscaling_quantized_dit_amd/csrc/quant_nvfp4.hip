@@ -11,11 +11,11 @@
 //
 // Dynamic mode is two passes: k_amax_partials writes one maximum per workgroup
 // (no zero-initialised state, no atomics), k_quant_nvfp4 folds those and encodes.
-// Both passes read with streaming (nt) loads and the encode pass stores the same
-// way.  (Ordinary loads in the amax pass, leaving a tensor of up to 256 MB in the
-// last-level cache for the encode pass, measured faster in isolation but 10 us
-// slower at 113 MB right after the step's GEMMs.)  The encode pass still takes
-// the slabs last to first.  Block scales go out row-major or in the GEMM-tiled
+// Both passes read with streaming (nt) loads.  (Ordinary loads in the amax pass,
+// leaving the tail of the tensor in the last-level cache for the encode pass,
+// measured faster in isolation but 6% slower at 113 MB and 16% at 566 MB right
+// after an NVFP4 GEMM.)  The encode pass still takes the slabs last to first, and
+// stores the codes with ordinary stores, since the GEMM reads them next.  Block scales go out row-major or in the GEMM-tiled
 // order (mxq_internal.h); for the latter a workgroup takes 64 rows x 128 values,
 // four rows per wave, so that each wave's scale bytes form one contiguous run.
 //
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
       const int u = g0 + i;
       const int64_t c = chunk(u);
       if (TILED || c < n_chunks) {
-        dev::store_nt(codes[i], q + c);
+        q[c] = codes[i];
         if ((t & 1) == 0) s[TILED ? ts.scale(u) : c >> 1] = (uint8_t)sb[i];
       }
     }
