@@ -55,6 +55,30 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t m) {
   return m;
 }
 
+// Maximum of n (1 <= n <= 256) partial maxima in two steps, with no LDS and no
+// barrier.  partial_loads: each lane loads four of them (indices clamped to n - 1,
+// so every load is unconditional and in bounds).  fold_wave: their maximum, then
+// the lanes of each row of 16 meet through DPP (pair swap, quad swap, half-row and
+// row mirrors) and the four row maxima are read out of lanes 0, 16, 32 and 48, so
+// the result is the same in every lane.  Every lane of the wave must be active.
+__device__ __forceinline__ uint4 partial_loads(const uint32_t* __restrict__ p, int n) {
+  const int l = threadIdx.x & 63;
+  const uint32_t last = (uint32_t)(n - 1);
+  return make_uint4(p[min((uint32_t)l, last)], p[min((uint32_t)l + 64u, last)], p[min((uint32_t)l + 128u, last)],
+                    p[min((uint32_t)l + 192u, last)]);
+}
+
+__device__ __forceinline__ uint32_t fold_wave(uint4 pl) {
+  uint32_t m = max(max(pl.x, pl.y), max(pl.z, pl.w));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));    // [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));    // [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));   // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // Pass 1: per-workgroup maximum of |x| (as 15-bit bf16 magnitude bits).
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_partials(const uint4* __restrict__ x, int64_t n_chunks,
                                                                 uint32_t* __restrict__ partials) {
@@ -186,7 +210,6 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
                                                           uint32_t* __restrict__ q, uint8_t* __restrict__ s,
                                                           float* __restrict__ global_out, int reverse,
                                                           ScaleTiling tiling) {
-  __shared__ uint32_t red[kThreads / 64];
   const int t = threadIdx.x;
   // with `reverse` workgroups take the slabs last to first: right after the amax
   // pass, what it read last is the likeliest to be left in a cache
@@ -194,6 +217,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
   const int64_t base = slab * (kThreads * kUnroll);
   const auto ts = TILED ? dev::TiledSlab<kUnroll, 8>((int)slab, t, tiling) : dev::TiledSlab<kUnroll, 8>();
   auto chunk = [&](int u) { return TILED ? ts.chunk(u) : base + u * kThreads + t; };
+  // dynamic mode: this lane's share of the partial maxima, loaded before the tensor
+  // so that the fold below need not wait for the tensor's loads
+  const uint4 pl = global_in ? make_uint4(0, 0, 0, 0) : partial_loads(partials, n_partials);
   uint4 v[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
@@ -201,27 +227,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
     v[u] = TILED || c < n_chunks ? dev::load_nt(x + c) : make_uint4(0, 0, 0, 0);
   }
 
-  // ---- the global decode scale s_g
+  // ---- the global decode scale s_g (every wave folds the partials itself)
   float sg;
   if (global_in) {
     sg = *global_in;
   } else {
-    uint32_t m = t < n_partials ? partials[t] : 0u;
-    m = wave_max(m);
-    if ((t & 63) == 0) red[t >> 6] = m;
-    __syncthreads();
-    uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
+    const uint32_t amax = fold_wave(pl);
     // IEEE (correctly rounded) fp32 division: RN_fp32(amax / 2688).
     sg = amax == 0 ? 1.0f : __uint_as_float(amax << 16) / 2688.0f;
   }
   if (slab == 0 && t == 0) *global_out = sg;
 
-  // ---- per-kernel constants: bracketing reciprocals of 6 s_g
-  const double six_sg = 6.0 * (double)sg;                   // exact (3 x 24 bits)
-  const double r6 = 1.0 / six_sg;
-  const float r6_lo = (float)(r6 * (1.0 - 0x1p-19));
-  const float r6_hi = (float)(r6 * (1.0 + 0x1p-19));
-  const bool fast6 = r6 < 0x1p126 && r6 > 0x1p-126;
+  // ---- per-kernel constants: bracketing reciprocals of 6 s_g.  fl(6 s_g) is within
+  // 2^-24 of 6 s_g and the hardware reciprocal within one ulp, so r6 is within
+  // ~2^-22.4 of 1/(6 s_g), far inside the 2^-19 nudges.  Outside fp32's normal
+  // range (including a zero, negative, infinite or NaN static s_g) the fp64 search
+  // decides.
+  const float r6 = __builtin_amdgcn_rcpf(6.0f * sg);
+  const float r6_lo = r6 * (1.0f - 0x1p-19f);
+  const float r6_hi = r6 * (1.0f + 0x1p-19f);
+  const bool fast6 = r6 < 0x1p126f && r6 > 0x1p-126f;
 
   // The chunks go through each phase in groups of kGroup, so that the fast path is
   // straight-line code and the exact fallbacks are entered once per phase and
@@ -257,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(const uint4* __restric
       for (int i = 0; i < kGroup; ++i) {
         const int cl = sb[i], ch = sb_hi[i];
         if (!fast6) {
-          sb[i] = exact_block_scale((double)amax_b[i], six_sg);
+          sb[i] = exact_block_scale((double)amax_b[i], 6.0 * (double)sg);   // 6 s_g exact in fp64
         } else if (cl != ch) {
           // one midpoint between the adjacent codes cl < ch: compare exactly
           const float mk = (__builtin_amdgcn_cvt_f32_fp8(cl, 0) + __builtin_amdgcn_cvt_f32_fp8(ch, 0)) * 3.0f;
