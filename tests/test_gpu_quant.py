@@ -177,6 +177,24 @@ def test_flux_single_stream_activation_nvfp4(mxq, cols):
     torch.cuda.empty_cache()
 
 
+# The amax pass writes one partial maximum per 4096 16-byte chunks (at most 256);
+# every wave of the encode pass folds all of them.  A tensor of [8P, 4096] has
+# exactly P partials; the tensor maximum (negative, so that the fold must use
+# magnitudes) sits in the first, a middle or the last of them, and with P not a
+# multiple of 64 some lanes fold clamped, repeated indices.
+@pytest.mark.parametrize("P", [1, 2, 63, 64, 65, 127, 129, 200, 255, 256])
+@pytest.mark.parametrize("where", ["first", "middle", "last"])
+def test_nvfp4_global_scale_every_partial_count(mxq, P, where):
+    R, C = 8 * P, 4096
+    n = R * C
+    bits = (0x3F80 + (np.arange(n, dtype=np.uint32) * 2654435761 >> 26) % 96).astype(np.uint16)
+    bits ^= ((np.arange(n) % 7 == 3).astype(np.uint16) << 15)                      # some negatives
+    at = {"first": 5, "middle": (P // 2) * 32768 + 1234, "last": n - 1}[where]
+    bits[at] = 0xC47A                                                              # -1000.0
+    bits = bits.reshape(R, C)
+    _check_nv(mxq, bits, rows=np.array(sorted({0, at // C, R - 1})))
+
+
 def test_deterministic(mxq):
     import torch
     x = _dev(inputs.flux_activation(512, 3072, seed=9, stream="det"))
