@@ -16,7 +16,8 @@ block, each preceded by the dynamic quantization of its bf16 activation:
 Weights are quantized once before timing (static, as in offline weight
 quantization); inputs are seeded synthetic tensors resident in HBM before the
 timed region.  value = GEMM flops of the step / step time (TFLOP/s).  Per-op
-times come from HIP events on the launch stream around every launch.  The CPU
+times come from HIP events on the launch stream around every launch (mean,
+median, 10th and 90th percentile over the timed steps).  The CPU
 oracle is timed on a bounded sample of the same work (cpu_baseline).
 
 Beside the step the line carries legs that are not part of it: measured_peaks
@@ -477,6 +478,16 @@ def static_scale_variant(torch, mxq, inputs, wl):
             "static_GB/s": round(rate, 1), "static_frac_of_hbm": round(rate / PEAK_HBM_GBPS, 4),
             "calibrated_scale": float(running[0])}
     return out
+
+
+def spread(samples):
+    """Median, 10th and 90th percentile (ms) of one op's per-step times; the three
+    are the same value when there is a single sample."""
+    if len(samples) < 2:
+        v = round(float(samples[0]), 4) if samples else None
+        return {"ms_median": v, "ms_p10": v, "ms_p90": v}
+    q = statistics.quantiles(samples, n=10, method="inclusive")
+    return {"ms_median": round(statistics.median(samples), 4), "ms_p10": round(q[0], 4), "ms_p90": round(q[8], 4)}
 
 
 def _interleaved_ms(torch, fns, rounds: int = 15, inner: int = 5):
@@ -955,7 +966,8 @@ def main():
 
     per_op = {}
     for i, (name, kind, _) in enumerate(ops):
-        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        samples = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        ms = sum(samples) / args.steps
         unit, amount = work[name]
         if unit == "flops":
             peak = PEAK_TFLOPS["fp8"] if kind == "gemm_mx" else PEAK_TFLOPS["fp4"]
@@ -967,6 +979,7 @@ def main():
         else:
             rate = amount / (ms * 1e-3) / 1e9
             per_op[name] = {"ms": round(ms, 4), "GB/s": round(rate, 1), "frac_of_hbm": round(rate / PEAK_HBM_GBPS, 4)}
+        per_op[name].update(spread(samples))
 
     gemm_flops = sum(a for u, a in work.values() if u == "flops")
     q_bytes = sum(a for u, a in work.values() if u == "bytes")

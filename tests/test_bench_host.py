@@ -159,3 +159,12 @@ def test_more_than_one_gpu_is_refused():
                        text=True, env=env, timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_per_op_spread(bench):
+    """Per-op median and 10th / 90th percentiles over the timed steps."""
+    s = bench.spread([float(v) for v in range(1, 12)])      # 1 .. 11
+    assert s == {"ms_median": 6.0, "ms_p10": 2.0, "ms_p90": 10.0}
+    assert bench.spread([0.25]) == {"ms_median": 0.25, "ms_p10": 0.25, "ms_p90": 0.25}
+    s = bench.spread([3.0, 1.0])
+    assert s["ms_p10"] <= s["ms_median"] <= s["ms_p90"] and s["ms_median"] == 2.0
