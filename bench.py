@@ -834,6 +834,18 @@ def fused_quantize_gemm(torch, mxq, inputs, wl, reps: int = 20):
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it (empty if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(rows_per_linear: int):
     """The oracle (as it is) on a bounded sample: `rows_per_linear` activation rows of
     every linear of the step, quantized (dynamic scales over the sampled rows) and
@@ -871,7 +883,7 @@ def cpu_baseline(rows_per_linear: int):
             oracle.linear(a, wdeq, float(np.float64(g) * np.float64(extra)))
         flops += 2 * rows_per_linear * N * K
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
             "sample": "%d activation rows of each of the 6 linears (quantize + dequantize + fp64 GEMM "
                       "against full weights dequantized beforehand), %.1f s" % (rows_per_linear, dt)}
 
